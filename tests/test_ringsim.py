@@ -1,0 +1,124 @@
+"""The ring-protocol simulator against the pages' statements and the closed form."""
+import json
+import os
+
+import pytest
+
+from oracle import ringsim as rs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_two_buffer_golden_trace():
+    with open(os.path.join(GOLDEN, "ring_two_buffer_trace.json")) as f:
+        g = json.load(f)
+    sched = rs.schedule(g["stages"], len(g["tiles"]))
+    assert [s[1] for s in sched] == g["buffers"]
+    assert [s[2] for s in sched] == g["full_wait_parity"]
+    # the empty wait awaits the previous lap: passes at once on the first lap
+    assert [s[3] for s in sched] == [p ^ 1 for p in g["full_wait_parity"]]
+
+
+def test_flag_wait_semantics():
+    # wait(0) passes after a 0->1 flip, wait(1) after a 1->0 flip
+    f = (0, 1, 0)
+    assert not rs._may_pass(f, 0) and rs._may_pass(f, 1)
+    f = rs._arrive(f, 1)
+    assert f[0] == 1 and rs._may_pass(f, 0) and not rs._may_pass(f, 1)
+    f = rs._arrive(f, 1)
+    assert f[0] == 0 and rs._may_pass(f, 1)
+    # a counter with 3 expected arrivals flips only on the third
+    g = (0, 3, 0)
+    g = rs._arrive(g, 3)
+    g = rs._arrive(g, 3)
+    assert g[0] == 0 and g[1] == 1
+    g = rs._arrive(g, 3)
+    assert g == (1, 3, 1)
+
+
+CASES = [(S, T, P, C) for S in (1, 2, 3, 4) for T in (1, 3, 6, 8) for P in (1, 2) for C in (1, 2, 4)
+         if not (T == 8 and P * C >= 8) and not (S >= 3 and T == 8 and C == 4)]
+
+
+@pytest.mark.parametrize("S,T,P,C", CASES)
+def test_exhaustive_interleavings_safe_and_live(S, T, P, C):
+    r = rs.explore(S, T, P, C)
+    assert r.violation is None, r.violation
+    assert not r.deadlock
+    assert r.max_lead <= S
+
+
+def test_random_schedules_long_runs():
+    for S, P, C in [(2, 1, 4), (3, 2, 4), (4, 1, 8), (6, 2, 2)]:
+        assert rs.random_runs(S, 64, P, C, runs=30, seed=S * 100 + C) is None
+
+
+@pytest.mark.parametrize("variant,expect", [
+    ("one_barrier", "deadlock"),
+    ("empty_same_parity", "deadlock"),
+    ("drop_release", "deadlock"),
+    ("slot_div2", "violation"),
+    ("no_empty_wait", "violation"),
+    ("full_parity_flipped", "violation"),
+])
+def test_negative_controls_are_caught(variant, expect):
+    r = rs.explore(2, 6, 1, 2, variant=variant)
+    if expect == "deadlock":
+        assert r.deadlock or r.violation is not None
+        assert r.deadlock
+    else:
+        assert r.violation is not None
+    assert rs.random_runs(2, 8, 1, 2, runs=50, seed=1, variant=variant) is not None
+
+
+def test_one_barrier_deadlocks_at_first_tile():
+    r = rs.explore(2, 4, 1, 1, variant="one_barrier")
+    assert r.deadlock and r.states < 10
+
+
+def test_fill_k_plus_2_while_draining_k_needs_three_stages():
+    # With S buffers a producer can have begun at most tile k + S - 1 while a
+    # consumer still holds tile k.
+    for S in (1, 2, 3, 4, 5):
+        r = rs.explore(S, 2 * S + 2, 1, 1)
+        lead = max(b - k for k, b in r.reach_pairs)
+        assert lead == S - 1, (S, lead)
+    # consumers on stage 0 while producers issue stage 3 (stages 1, 2 full): S >= 4
+    assert (0, 3) not in rs.explore(3, 8, 1, 1).reach_pairs
+    assert (0, 3) in rs.explore(4, 8, 1, 1).reach_pairs
+
+
+@pytest.mark.parametrize("S,L,c", [(2, 3.0, 1.0), (2, 0.5, 1.0), (4, 3.0, 1.0), (6, 3.0, 1.0),
+                                   (3, 7.3, 2.1), (8, 30.0, 1.0)])
+def test_timed_matches_closed_form(S, L, c):
+    T = max(200, 100 * S)
+    tl = rs.timed(S, T, L, c)
+    assert tl.period() == pytest.approx(rs.steady_period(S, L, c), rel=0.01)
+
+
+def test_shallow_ring_stalls_and_deep_ring_does_not():
+    L, c = 5.0, 1.0
+    shallow = rs.timed(2, 400, L, c)
+    deep = rs.timed(rs.min_stages(L, c), 400, L, c)
+    assert shallow.consumer_wait > 100 * c
+    assert deep.consumer_wait <= L + c  # only the fill
+    assert rs.min_stages(L, c) == 6  # S >= 1 + L / c
+    # compute bound: in steady state the producer waits on free buffers
+    assert deep.producer_wait > 0
+
+
+def test_early_release_shortens_the_ring():
+    # releasing a buffer once its data is in registers (r < c) needs fewer stages
+    assert rs.min_stages(3.5, 1.0, release_after=0.25) == 4
+    assert rs.min_stages(3.5, 1.0) == 5
+    tl = rs.timed(4, 400, 3.5, 1.0, release_after=0.25)
+    assert tl.period() == pytest.approx(1.0, rel=0.01)
+    tl = rs.timed(4, 400, 3.5, 1.0)
+    assert tl.period() == pytest.approx(rs.steady_period(4, 3.5, 1.0), rel=0.01) and tl.period() > 1.1
+
+
+def test_jitter_keeps_order_and_bounds():
+    tl = rs.timed(3, 300, 4.0, 1.0, jitter=1.0, seed=3)
+    assert all(tl.start[i] >= tl.land[i] for i in range(300))
+    assert all(tl.start[i] >= tl.end[i - 1] for i in range(1, 300))
+    assert all(tl.issue[i] >= tl.release[i - 3] for i in range(3, 300))
