@@ -1,0 +1,147 @@
+/*
+ * wsg.h - C ABI of libwsg.so: a wave-specialized GEMM with a fused bias + ReLU
+ * epilogue and an LDS-staged copy, for AMD MI355X (gfx950).
+ *
+ * Sources (three web pages on warp specialization):
+ *   [KP] pwwt.cn/news/4436243, Chinese article on intra-kernel pipelining
+ *        with TMA and mbarrier; section 4.1 defines the operator: float
+ *        A[M,K], B[K,N], C[M,N] = A*B + bias followed by a ReLU; sections
+ *        3.2-3.4 describe producer and consumer warps joined by a ring of
+ *        shared-memory stages with a full and an empty barrier per stage.
+ *   [WS] aicassindra.com, "GPU warp specialization"; "End-to-end flow": one
+ *        output tile per block, K-dimension tiles of A and B streamed through
+ *        an N-stage ring by producer warps while consumer warps accumulate.
+ *   [PC] willy-chan.github.io, "Producer-Consumer Warp Specialization for
+ *        TMA Operations": a double-buffered load into shared memory and store
+ *        back out to global memory, tile i in buffer i mod 2, waits on the
+ *        parity of i / 2.
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no memory for them and keeps no pointer after returning.
+ *   - Launches are asynchronous on the calling thread's stream (see
+ *     wsg_set_stream); the caller keeps buffers alive and synchronizes before
+ *     reading results, as with any stream API.
+ *   - Matrices are dense row-major: A[m*K + k], B[k*N + n], C[m*N + n];
+ *     bias has N entries, one per output column.
+ *   - Return codes: WSG_OK, or a negative WSG_E* code; wsg_last_error()
+ *     then returns a description (thread-local).
+ */
+#ifndef WSG_H
+#define WSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WSG_OK 0
+#define WSG_EINVAL (-1)       /* invalid argument: negative size, null or misaligned pointer, overlap, stages < 1 */
+#define WSG_EUNSUPPORTED (-2) /* configuration the device cannot run: LDS over the per-workgroup limit, tile or wave
+                                 combination not built, sizes beyond the 32-bit offsets of a tile */
+#define WSG_ELAUNCH (-3)      /* HIP runtime error while launching; see wsg_last_error() */
+#define WSG_ETIMEOUT (-4)     /* a bounded flag wait on the device gave up (reported by wsg_check_device_status) */
+
+/* dtype codes for wsg_gemm_bias_relu_ex / wsg_gemm_resolve_config */
+#define WSG_FP32 0
+#define WSG_BF16 1
+
+/* flags for wsg_config.flags */
+#define WSG_FLAG_GENERAL_PRODUCER 1 /* force the register-staged producer (any shape) over the LDS-DMA one */
+
+/*
+ * Launch configuration. A zero field means "choose the default". The
+ * workgroup runs producer_waves + consumer_waves wavefronts of 64 lanes.
+ */
+typedef struct wsg_config {
+    int BM, BN, BK;       /* GEMM workgroup tile: rows of C, columns of C, k per ring slot */
+    int producer_waves;   /* waves that fill the ring */
+    int consumer_waves;   /* waves that drain it (GEMM: run the MFMAs; copy: store to dst) */
+    int copy_tile_bytes;  /* staged copy: bytes per ring slot (default 65536) */
+    int flags;            /* WSG_FLAG_* */
+} wsg_config;
+
+/*
+ * C = relu(A @ B + bias), fp32 operands and output, fp32 MFMA with fp32
+ * accumulation ([KP] section 4.1). The K loop runs through an LDS ring of
+ * `stages` slots: producer waves load K-tiles of A and B into slot t mod S
+ * and mark it full; consumer waves wait for it with parity (t / S) & 1,
+ * multiply, and mark it empty ([WS] "End-to-end flow"; [PC]).
+ *   M, N, K  >= 0. M == 0 or N == 0: nothing written. K == 0: C = relu(bias).
+ *   A        M x K, B K x N, bias N, C M x N; 4-byte aligned; C must not
+ *            overlap A, B or bias.
+ *   stages   ring depth S >= 1; S beyond what fits in LDS -> WSG_EUNSUPPORTED.
+ * relu(x) is x for x > 0, NaN for NaN, +0 otherwise. Any M, N, K are
+ * accepted; out-of-range rows, columns and k are zero-filled by the producer.
+ */
+int gemm_bias_relu(int64_t M, int64_t N, int64_t K, const float *A, const float *B, const float *bias,
+                   float *C, int stages);
+
+/*
+ * The same operator with bf16 operands and bias (raw bf16 bit patterns,
+ * 2-byte aligned), bf16 MFMA with fp32 accumulation, fp32 output C.
+ */
+int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
+                        const uint16_t *bias, float *C, int stages);
+
+/*
+ * Either GEMM with an explicit launch configuration (cfg may be NULL).
+ * dtype is WSG_FP32 (A, B, bias are float*) or WSG_BF16 (uint16_t* bits).
+ */
+int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                      const void *bias, float *C, int stages, const wsg_config *cfg);
+
+/*
+ * The configuration gemm_bias_relu_ex would launch for these arguments,
+ * written to *out, after the same validation (returns its error code).
+ * Writes the resolved tile and wave counts; no device work.
+ */
+int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stages, const wsg_config *cfg,
+                            wsg_config *out);
+
+/*
+ * dst[0:bytes] = src[0:bytes], staged through a ring of `stages` LDS slots
+ * ([PC]): producer waves load a tile into slot j mod S and mark it full;
+ * consumer waves wait on its parity, copy it out to dst and mark it empty.
+ *   src, dst  device pointers, 16-byte aligned, non-overlapping (else
+ *             WSG_EINVAL); any byte count, bytes == 0 is a no-op.
+ *   stages    S >= 1; S * tile bytes must fit in LDS (else WSG_EUNSUPPORTED,
+ *             e.g. 3 x 64 KiB).
+ * Bits move as integers: NaN payloads and -0 are preserved.
+ */
+int staged_copy(const void *src, void *dst, size_t bytes, int stages);
+
+/* staged_copy with an explicit configuration (copy_tile_bytes, wave counts; cfg may be NULL). */
+int staged_copy_ex(const void *src, void *dst, size_t bytes, int stages, const wsg_config *cfg);
+
+/*
+ * Stream used by this thread's later launches (a hipStream_t; NULL = the
+ * default stream). Thread-local. Returns WSG_OK.
+ */
+int wsg_set_stream(void *hip_stream);
+
+/* The calling thread's current stream (as set by wsg_set_stream). */
+void *wsg_get_stream(void);
+
+/* Text describing the calling thread's last nonzero return code ("" if none). */
+const char *wsg_last_error(void);
+
+/*
+ * Synchronizes the calling thread's stream, then reads and clears the
+ * current device's status word. Every flag wait in the kernels gives up after
+ * a bounded number of polls (so a protocol fault ends the kernel instead of
+ * hanging the GPU) and records it there. Returns WSG_OK, WSG_ETIMEOUT, or
+ * WSG_ELAUNCH if synchronization failed.
+ */
+int wsg_check_device_status(void);
+
+/* Library version string. */
+const char *wsg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WSG_H */

@@ -1,0 +1,107 @@
+"""The C-ABI library loads and exports every function include/wsg.h declares.
+
+No compute calls: only argument checks that return before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wsg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def wsg():
+    import warp_specialized_gemm_amd as w
+    return w
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ("gemm_bias_relu", "gemm_bias_relu_bf16", "staged_copy", "gemm_bias_relu_ex", "staged_copy_ex",
+              "wsg_set_stream", "wsg_last_error", "wsg_check_device_status"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(wsg):
+    names = declared_functions()
+    assert sorted(wsg.EXPORTS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", wsg.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(wsg.lib, n)
+
+
+def test_library_is_gfx950_code(wsg):
+    data = open(wsg.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def test_version(wsg):
+    assert "gfx950" in wsg.version()
+
+
+def test_invalid_arguments_rejected_before_any_device_call(wsg):
+    L = wsg.lib
+    nul = None
+    # negative dimension
+    assert L.gemm_bias_relu(-1, 4, 4, nul, nul, nul, nul, 2) == wsg.WSG_EINVAL
+    assert "negative" in wsg.last_error()
+    # stages < 1
+    assert L.gemm_bias_relu(4, 4, 4, 16, 16, 16, 16, 0) == wsg.WSG_EINVAL
+    # null operands with nonzero sizes
+    assert L.gemm_bias_relu(4, 4, 4, nul, nul, nul, nul, 2) == wsg.WSG_EINVAL
+    # misaligned fp32 operand
+    assert L.gemm_bias_relu(4, 4, 4, 0x1002, 0x2000, 0x3000, 0x40000, 2) == wsg.WSG_EINVAL
+    # C overlapping A
+    assert L.gemm_bias_relu(4, 4, 4, 0x10000, 0x20000, 0x30000, 0x10010, 2) == wsg.WSG_EINVAL
+    assert "overlap" in wsg.last_error()
+    # dtype code
+    assert L.gemm_bias_relu_ex(7, 4, 4, 4, 0x10000, 0x20000, 0x30000, 0x40000, 2, None) == wsg.WSG_EINVAL
+    # dimensions beyond 31 bits
+    assert L.gemm_bias_relu(1 << 31, 4, 4, 0x10000, 0x20000, 0x30000, 0x40000, 2) == wsg.WSG_EUNSUPPORTED
+    # empty problems are no-ops that succeed
+    assert L.gemm_bias_relu(0, 4, 4, nul, nul, nul, nul, 2) == wsg.WSG_OK
+    assert L.gemm_bias_relu(4, 0, 4, nul, nul, nul, nul, 2) == wsg.WSG_OK
+    # copy: zero bytes, null, misaligned, overlapping, stages
+    assert L.staged_copy(nul, nul, 0, 2) == wsg.WSG_OK
+    assert L.staged_copy(nul, 0x1000, 16, 2) == wsg.WSG_EINVAL
+    assert L.staged_copy(0x1008, 0x2000, 16, 2) == wsg.WSG_EINVAL
+    assert L.staged_copy(0x1000, 0x1010, 64, 2) == wsg.WSG_EINVAL
+    assert "overlap" in wsg.last_error()
+    assert L.staged_copy(0x1000, 0x9000, 64, 0) == wsg.WSG_EINVAL
+
+
+def test_stream_is_thread_local(wsg):
+    import threading
+    wsg.lib.wsg_set_stream(ctypes.c_void_p(0x1234))
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(wsg.lib.wsg_get_stream()))
+    t.start()
+    t.join()
+    assert wsg.lib.wsg_get_stream() == 0x1234
+    assert seen == [None]
+    wsg.lib.wsg_set_stream(None)
+    assert wsg.lib.wsg_get_stream() is None
+
+
+def test_config_struct_layout_matches_header(wsg):
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct wsg_config \{(.*?)\} wsg_config;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"([A-Za-z_]+)\s*[,;]", body)
+    assert fields == [f for f, _ in wsg.Config._fields_]
+    assert ctypes.sizeof(wsg.Config) == 4 * len(fields)

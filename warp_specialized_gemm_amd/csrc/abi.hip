@@ -1,0 +1,205 @@
+// abi.hip - the extern "C" entry points declared in include/wsg.h: argument
+// validation, per-device state, the calling thread's stream and last error.
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "ring.hpp"
+
+// Device status word; each GPU holds its own copy. Kernels get its device
+// address (looked up per device with hipGetSymbolAddress) as an argument.
+__device__ unsigned wsg_status_word;
+
+namespace {
+
+thread_local hipStream_t tl_stream = nullptr;
+thread_local std::string tl_err;
+
+std::mutex g_mu;
+std::vector<wsg::DeviceInfo> g_devs;
+
+int fail(int code, const std::string &msg) {
+    tl_err = msg;
+    return code;
+}
+
+int ok() {
+    tl_err.clear();
+    return WSG_OK;
+}
+
+int device_info(wsg::DeviceInfo *out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_mu);
+    if ((int)g_devs.size() <= dev) g_devs.resize(dev + 1);
+    wsg::DeviceInfo &d = g_devs[dev];
+    if (d.device < 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+        if (std::string(prop.gcnArchName).rfind("gfx950", 0) != 0)
+            return fail(WSG_EUNSUPPORTED, std::string("libwsg is built for gfx950 only; device is ") + prop.gcnArchName);
+        int lds = 0;
+        e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(wsg_status_word));
+        if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+        d.cu_count = prop.multiProcessorCount;
+        d.max_lds = (size_t)lds;
+        d.status = static_cast<unsigned *>(p);
+        d.device = dev;
+    }
+    *out = d;
+    return WSG_OK;
+}
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    if (!an || !bn) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
+                  const float *C, int stages) {
+    if (dtype != WSG_FP32 && dtype != WSG_BF16) return fail(WSG_EINVAL, "dtype must be WSG_FP32 or WSG_BF16");
+    if (M < 0 || N < 0 || K < 0) return fail(WSG_EINVAL, "negative dimension");
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WSG_EUNSUPPORTED, "dimension above 2^31 - 1");
+    if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
+    if (M == 0 || N == 0) return WSG_OK;
+    const size_t esz = dtype == WSG_FP32 ? 4 : 2;
+    if (K > 0 && (!A || !B)) return fail(WSG_EINVAL, "null A or B with a nonzero size");
+    if (!bias || !C) return fail(WSG_EINVAL, "null bias or C with a nonzero size");
+    if (((uintptr_t)A % esz) || ((uintptr_t)B % esz) || ((uintptr_t)bias % esz))
+        return fail(WSG_EINVAL, "A, B and bias must be aligned to their element size");
+    if ((uintptr_t)C % 4) return fail(WSG_EINVAL, "C must be 4-byte aligned");
+    const size_t cbytes = (size_t)M * (size_t)N * 4;
+    if (overlaps(C, cbytes, A, (size_t)M * (size_t)K * esz) || overlaps(C, cbytes, B, (size_t)K * (size_t)N * esz) ||
+        overlaps(C, cbytes, bias, (size_t)N * esz))
+        return fail(WSG_EINVAL, "C overlaps an input");
+    return WSG_OK;
+}
+
+int gemm_impl(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, float *C,
+              int stages, const wsg_config *cfg) {
+    int rc = validate_gemm(dtype, M, N, K, A, B, bias, C, stages);
+    if (rc != WSG_OK) return rc;
+    if (M == 0 || N == 0) return ok();
+    wsg::LaunchCtx ctx;
+    rc = device_info(&ctx.dev);
+    if (rc != WSG_OK) return rc;
+    ctx.stream = tl_stream;
+    wsg::GemmPlan plan;
+    std::string err;
+    rc = wsg::plan_gemm(dtype, M, N, K, A, B, stages, cfg, ctx.dev, &plan, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    rc = wsg::launch_gemm(ctx, plan, M, N, K, A, B, bias, C, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    return ok();
+}
+
+int copy_impl(const void *src, void *dst, size_t bytes, int stages, const wsg_config *cfg) {
+    if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(WSG_EINVAL, "null src or dst with a nonzero size");
+    if (((uintptr_t)src % 16) || ((uintptr_t)dst % 16)) return fail(WSG_EINVAL, "src and dst must be 16-byte aligned");
+    if (overlaps(src, bytes, dst, bytes)) return fail(WSG_EINVAL, "src and dst overlap");
+    wsg::LaunchCtx ctx;
+    int rc = device_info(&ctx.dev);
+    if (rc != WSG_OK) return rc;
+    ctx.stream = tl_stream;
+    wsg::CopyPlan plan;
+    std::string err;
+    rc = wsg::plan_copy(bytes, stages, cfg, ctx.dev, &plan, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    rc = wsg::launch_copy(ctx, plan, src, dst, bytes, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bias_relu(int64_t M, int64_t N, int64_t K, const float *A, const float *B, const float *bias, float *C,
+                   int stages) {
+    return gemm_impl(WSG_FP32, M, N, K, A, B, bias, C, stages, nullptr);
+}
+
+int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                        float *C, int stages) {
+    return gemm_impl(WSG_BF16, M, N, K, A, B, bias, C, stages, nullptr);
+}
+
+int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
+                      float *C, int stages, const wsg_config *cfg) {
+    return gemm_impl(dtype, M, N, K, A, B, bias, C, stages, cfg);
+}
+
+int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stages, const wsg_config *cfg,
+                            wsg_config *out) {
+    if (!out) return fail(WSG_EINVAL, "null output config");
+    if (dtype != WSG_FP32 && dtype != WSG_BF16) return fail(WSG_EINVAL, "dtype must be WSG_FP32 or WSG_BF16");
+    if (M < 0 || N < 0 || K < 0) return fail(WSG_EINVAL, "negative dimension");
+    if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
+    wsg::DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != WSG_OK) return rc;
+    wsg::GemmPlan plan;
+    std::string err;
+    // 16-byte aligned operands are assumed, as from any device allocator
+    rc = wsg::plan_gemm(dtype, M, N, K, nullptr, nullptr, stages, cfg, dev, &plan, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    out->BM = plan.v->BM;
+    out->BN = plan.v->BN;
+    out->BK = plan.v->BK;
+    out->producer_waves = plan.v->P;
+    out->consumer_waves = plan.v->CWM * plan.v->CWN;
+    out->copy_tile_bytes = 0;
+    out->flags = plan.v->dma ? 0 : WSG_FLAG_GENERAL_PRODUCER;
+    return ok();
+}
+
+int staged_copy(const void *src, void *dst, size_t bytes, int stages) {
+    return copy_impl(src, dst, bytes, stages, nullptr);
+}
+
+int staged_copy_ex(const void *src, void *dst, size_t bytes, int stages, const wsg_config *cfg) {
+    return copy_impl(src, dst, bytes, stages, cfg);
+}
+
+int wsg_set_stream(void *hip_stream) {
+    tl_stream = static_cast<hipStream_t>(hip_stream);
+    return ok();
+}
+
+void *wsg_get_stream(void) { return tl_stream; }
+
+const char *wsg_last_error(void) { return tl_err.c_str(); }
+
+int wsg_check_device_status(void) {
+    wsg::DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != WSG_OK) return rc;
+    hipError_t e = hipStreamSynchronize(tl_stream);
+    if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    unsigned word = 0, zero = 0;
+    e = hipMemcpy(&word, dev.status, sizeof word, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(dev.status, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("status word copy: ") + hipGetErrorString(e));
+    if (word & wsg::kStatusTimeout) {
+        std::string who = (word & wsg::kStatusCopy) ? "staged_copy" : "";
+        if (word & wsg::kStatusGemm) who += who.empty() ? "gemm" : " and gemm";
+        return fail(WSG_ETIMEOUT, "a ring flag wait gave up in " + who + " (protocol fault)");
+    }
+    return ok();
+}
+
+const char *wsg_version(void) { return "wsg 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// internal.hpp - host-side declarations shared by the library's translation
+// units (not part of the public ABI; see include/wsg.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/wsg.h"
+
+namespace wsg {
+
+struct DeviceInfo {
+    int device = -1;
+    int cu_count = 0;
+    size_t max_lds = 0;  // bytes of LDS one workgroup may allocate
+    unsigned *status = nullptr;  // device address of the status word
+};
+
+struct LaunchCtx {
+    hipStream_t stream = nullptr;
+    DeviceInfo dev;
+};
+
+// One compiled GEMM variant.
+struct GemmVariant {
+    int dtype;    // WSG_FP32 / WSG_BF16
+    int BM, BN, BK;
+    int P;        // producer waves
+    int CWM, CWN; // consumer wave grid
+    bool dma;     // LDS-DMA producer (aligned shapes) or register-staged producer (any shape)
+    const void *kernel;
+};
+
+struct GemmPlan {
+    const GemmVariant *v = nullptr;
+    int stages = 0;
+    int64_t tiles_m = 0, tiles_n = 0;
+    size_t lds_bytes = 0;
+};
+
+struct CopyPlan {
+    int P = 0, C = 0, tile = 0, stages = 0;
+    const void *kernel = nullptr;
+    size_t lds_bytes = 0;
+};
+
+// Fill `plan` for the arguments; returns WSG_OK or an error code with `err` set.
+int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, int stages,
+              const wsg_config *cfg, const DeviceInfo &dev, GemmPlan *plan, std::string *err);
+int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N, int64_t K, const void *A,
+                const void *B, const void *bias, float *C, std::string *err);
+
+int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo &dev, CopyPlan *plan,
+              std::string *err);
+int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, void *dst, size_t bytes,
+                std::string *err);
+
+}  // namespace wsg

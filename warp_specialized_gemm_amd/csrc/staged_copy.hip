@@ -1,0 +1,221 @@
+// staged_copy.hip - HBM -> LDS ring -> HBM copy with producer and consumer
+// waves ("Producer-Consumer Warp Specialization for TMA Operations": a
+// double-buffered load into shared memory and a store back out, where the
+// full flag trips as data flows into a buffer and the empty flag as it flows
+// out).
+//
+// Work split: a persistent grid of G workgroups (one per CU: two 64 KiB slots
+// take most of the 160 KiB of LDS); workgroup g copies tiles g, g + G, ...,
+// and its j-th tile uses slot j mod S with wait parity (j / S) & 1.
+//
+// Producer waves issue 16-byte LDS-DMA loads (global -> LDS, no VGPRs) for a
+// tile and keep up to S - 1 further tiles in flight before they mark a tile
+// full (vmcnt counts loads in issue order). Consumer waves wait full, read
+// the slot into VGPRs, release it as soon as those reads completed, then
+// store to dst. Data moves as raw bits throughout.
+#include "internal.hpp"
+#include "ring.hpp"
+
+namespace wsg {
+
+template <int P, int C, int TILE>
+__global__ void __launch_bounds__((P + C) * 64)
+    staged_copy_kernel(const unsigned char *__restrict__ src, unsigned char *__restrict__ dst, uint64_t bytes,
+                       uint64_t ntiles, int S, unsigned *status) {
+    static_assert(TILE % (P * 1024) == 0 && TILE % (C * 1024) == 0, "tile must split into 1 KiB wave chunks");
+    constexpr int NL = TILE / (P * 1024);  // LDS-DMA loads per producer wave per tile
+    constexpr int NC = TILE / (C * 1024);  // 16-byte reads per consumer lane per tile
+    static_assert(NL <= 63, "a tile's loads must fit the vmcnt counter");
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *ring = lds + kFlagBytes;
+    const uint32_t fb = lds_addr(lds);
+    const int wave = wave_id();
+    const int lane = lane_id();
+
+    if (threadIdx.x < kFlagBytes / 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0u;
+    __syncthreads();  // the only workgroup barrier: flags start at phase 0
+
+    const uint64_t G = gridDim.x;
+    const uint64_t g = blockIdx.x;
+    if (g >= ntiles) return;
+    const int64_t nloc = (int64_t)((ntiles - g + G - 1) / G);  // tiles of this workgroup
+
+    if (wave < P) {
+        // ---------------- producer ----------------
+        const int D = min(S - 1, 63 / NL);  // tiles kept in flight beyond the one being completed
+        auto finish = [&](int64_t j) {
+            const int s = (int)(j % S);
+            const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
+            const uint64_t valid = min((uint64_t)TILE, bytes - base);
+            if ((valid & 15u) && wave == 0) {
+                // bytes past the last whole 16-byte chunk: byte loads into the slot
+                const uint64_t v16 = valid & ~(uint64_t)15;
+                if ((uint64_t)lane < (valid - v16)) {
+                    unsigned char b = src[base + v16 + lane];
+                    ring[(size_t)s * TILE + v16 + lane] = b;
+                }
+                wait_vmcnt<0>();
+                wait_lgkm0();
+            }
+            flag_arrive(full_flag(fb, s), P);
+        };
+        int s = 0;
+        uint32_t lap = 0;
+        for (int64_t j = 0; j < nloc; ++j) {
+            if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, status, kStatusCopy)) return;
+            const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
+            const uint64_t valid = min((uint64_t)TILE, bytes - base);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + base, (uint32_t)(valid & ~(uint64_t)15));
+            unsigned char *slot = ring + (size_t)s * TILE;
+#pragma unroll
+            for (int r = 0; r < NL; ++r) {
+                const uint32_t off = (uint32_t)(r * P + wave) * 1024u;
+                lds_dma16(rs, slot + off, off + 16u * lane);
+            }
+            if (j >= D) {
+                wait_vmcnt_dyn(D * NL);
+                finish(j - D);
+            }
+            if (++s == S) {
+                s = 0;
+                ++lap;
+            }
+        }
+        for (int64_t j = max((int64_t)0, nloc - D); j < nloc; ++j) {
+            wait_vmcnt_dyn((int)(nloc - 1 - j) * NL);
+            finish(j);
+        }
+    } else {
+        // ---------------- consumer ----------------
+        const int cw = wave - P;
+        int s = 0;
+        uint32_t lap = 0;
+        for (int64_t j = 0; j < nloc; ++j) {
+            if (!flag_wait(full_flag(fb, s), lap & 1u, status, kStatusCopy)) return;
+            const unsigned char *slot = ring + (size_t)s * TILE;
+            uint4 v[NC];
+#pragma unroll
+            for (int r = 0; r < NC; ++r)
+                v[r] = *reinterpret_cast<const uint4 *>(slot + (size_t)(r * C + cw) * 1024u + 16u * lane);
+            wait_lgkm0();
+            flag_arrive(empty_flag(fb, s), C);
+            const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
+            const uint64_t valid = min((uint64_t)TILE, bytes - base);
+            unsigned char *out = dst + base;
+            if (valid == (uint64_t)TILE) {
+#pragma unroll
+                for (int r = 0; r < NC; ++r)
+                    *reinterpret_cast<uint4 *>(out + (size_t)(r * C + cw) * 1024u + 16u * lane) = v[r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < NC; ++r) {
+                    const uint64_t off = (uint64_t)(r * C + cw) * 1024u + 16u * lane;
+                    if (off + 16 <= valid) {
+                        *reinterpret_cast<uint4 *>(out + off) = v[r];
+                    } else if (off < valid) {
+                        const uint32_t words[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+                        const uint32_t n = (uint32_t)(valid - off);
+#pragma unroll
+                        for (uint32_t i = 0; i < 16; ++i)
+                            if (i < n) out[off + i] = (unsigned char)(words[i >> 2] >> (8 * (i & 3)));
+                    }
+                }
+            }
+            if (++s == S) {
+                s = 0;
+                ++lap;
+            }
+        }
+    }
+}
+
+namespace {
+
+struct CopyVariant {
+    int P, C, tile;
+    const void *kernel;
+};
+
+#define WSG_COPY_VARIANT(P, C, T) {P, C, T, reinterpret_cast<const void *>(&staged_copy_kernel<P, C, T>)}
+
+const CopyVariant kCopyVariants[] = {
+    WSG_COPY_VARIANT(4, 4, 65536), WSG_COPY_VARIANT(2, 2, 65536), WSG_COPY_VARIANT(8, 8, 65536),
+    WSG_COPY_VARIANT(4, 8, 65536), WSG_COPY_VARIANT(4, 4, 32768), WSG_COPY_VARIANT(2, 2, 32768),
+    WSG_COPY_VARIANT(2, 2, 16384), WSG_COPY_VARIANT(1, 1, 16384), WSG_COPY_VARIANT(1, 1, 4096),
+};
+
+}  // namespace
+
+int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo &dev, CopyPlan *plan,
+              std::string *err) {
+    (void)bytes;
+    int tile = (cfg && cfg->copy_tile_bytes) ? cfg->copy_tile_bytes : 65536;
+    int P = (cfg && cfg->producer_waves) ? cfg->producer_waves : 0;
+    int C = (cfg && cfg->consumer_waves) ? cfg->consumer_waves : 0;
+    if (stages < 1) {
+        *err = "stages must be >= 1";
+        return WSG_EINVAL;
+    }
+    if (stages > kMaxStages) {
+        *err = "stages above the flag area's limit of " + std::to_string(kMaxStages);
+        return WSG_EUNSUPPORTED;
+    }
+    const CopyVariant *pick = nullptr;
+    for (const CopyVariant &v : kCopyVariants) {
+        if (v.tile != tile) continue;
+        if (P && v.P != P) continue;
+        if (C && v.C != C) continue;
+        pick = &v;
+        break;
+    }
+    if (!pick) {
+        *err = "no staged-copy kernel built for tile " + std::to_string(tile) + " bytes, " + std::to_string(P) +
+               " producer and " + std::to_string(C) + " consumer waves";
+        return WSG_EUNSUPPORTED;
+    }
+    size_t lds = (size_t)kFlagBytes + (size_t)stages * (size_t)tile;
+    if (lds > dev.max_lds) {
+        *err = "ring needs " + std::to_string(lds) + " bytes of LDS, the device allows " +
+               std::to_string(dev.max_lds) + " per workgroup";
+        return WSG_EUNSUPPORTED;
+    }
+    plan->P = pick->P;
+    plan->C = pick->C;
+    plan->tile = pick->tile;
+    plan->stages = stages;
+    plan->kernel = pick->kernel;
+    plan->lds_bytes = lds;
+    return WSG_OK;
+}
+
+int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, void *dst, size_t bytes,
+                std::string *err) {
+    if (bytes == 0) return WSG_OK;
+    const uint64_t ntiles = (bytes + (uint64_t)plan.tile - 1) / (uint64_t)plan.tile;
+    const int threads = (plan.P + plan.C) * 64;
+    hipError_t e = hipFuncSetAttribute(plan.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
+    if (e != hipSuccess) {
+        *err = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
+        return WSG_ELAUNCH;
+    }
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, plan.kernel, threads, plan.lds_bytes);
+    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    uint64_t grid = (uint64_t)ctx.dev.cu_count * (uint64_t)per_cu;
+    if (grid > ntiles) grid = ntiles;
+    const unsigned char *s = static_cast<const unsigned char *>(src);
+    unsigned char *d = static_cast<unsigned char *>(dst);
+    uint64_t nb = bytes;
+    int S = plan.stages;
+    unsigned *status = ctx.dev.status;
+    void *args[] = {&s, &d, &nb, (void *)&ntiles, &S, &status};
+    e = hipLaunchKernel(plan.kernel, dim3((unsigned)grid), dim3(threads), args, plan.lds_bytes, ctx.stream);
+    if (e != hipSuccess) {
+        *err = std::string("staged_copy launch: ") + hipGetErrorString(e);
+        return WSG_ELAUNCH;
+    }
+    return WSG_OK;
+}
+
+}  // namespace wsg
