@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X: prints ONE JSON line.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+one fp32 GEMM + bias + ReLU (M = N = K = 4096, uniform[-1,1), 4-stage ring,
+default launch configuration) and one LDS-staged copy of 1 GiB of fp32
+(64 KiB tiles, 2-stage ring). Inputs are generated on the host, copied to
+HBM and resident before timing starts.
+
+W untimed warmup steps, then K timed steps. The GEMMs and the copies are
+timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
+(and HIP events on the launch stream for the per-launch kernel durations):
+  value                = GEMM TFLOP/s over its timed region (2*M*N*K per launch)
+  copy.value           = copy GB/s over its timed region (2 * bytes per launch)
+  roofline             = the GEMM kernel against the fp32 MFMA peak
+  copy_roofline        = the copy kernel against the HBM peak
+  cpu_baseline         = the CPU oracle on a bounded sample of the same GEMM
+Options select other workloads (--workload 4: ragged fp32, --workload 5:
+bf16 8192^3) or a launch configuration (--stages, --bm/--bn/--bk,
+--producers, --consumers); --sweep prints one line per stage/producer point.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"fp32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gemm": ["warp_specialized_gemm_amd/csrc/gemm_bias_relu.hip", "warp_specialized_gemm_amd/csrc/ring.hpp"],
+    "copy": ["warp_specialized_gemm_amd/csrc/staged_copy.hip", "warp_specialized_gemm_amd/csrc/ring.hpp"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_hash") != source_hash(kind):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_gemm_inputs(wid: int):
+    import numpy as np
+    import synth
+    w = synth.WORKLOADS[wid]
+    M, N, K = w["M"], w["N"], w["K"]
+    if w["dtype"] == "fp32":
+        A = synth.uniform_pm1(synth.seed_for(wid, "A"), M * K).reshape(M, K)
+        B = synth.uniform_pm1(synth.seed_for(wid, "B"), K * N).reshape(K, N)
+        bias = synth.uniform_pm1(synth.seed_for(wid, "bias"), N)
+    else:
+        A = synth.normal_bf16_bits(synth.seed_for(wid, "A"), M * K).reshape(M, K)
+        B = synth.normal_bf16_bits(synth.seed_for(wid, "B"), K * N).reshape(K, N)
+        bias = synth.normal_bf16_bits(synth.seed_for(wid, "bias"), N)
+    return w, A, B, bias
+
+
+def gemm_launcher(wsg, w, dA, dB, dbias, dC, stages, config):
+    if w["dtype"] == "fp32" and config is None:
+        return lambda: wsg.gemm_bias_relu(dA, dB, dbias, dC, stages=stages)
+    if w["dtype"] == "bf16" and config is None:
+        return lambda: wsg.gemm_bias_relu_bf16(dA, dB, dbias, dC, stages=stages)
+    return lambda: wsg.gemm_bias_relu_ex(dA, dB, dbias, dC, stages=stages, config=config)
+
+
+def time_region(torch, fn, steps: int):
+    """Wall time of `steps` launches between two synchronizations, and the
+    mean per-launch kernel time from HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return wall, sum(per) / len(per), min(per)
+
+
+def cpu_baseline_gemm(A, B, bias, budget_s: float):
+    """The oracle on the first rows of the same GEMM, 16 rows at a time, until
+    about budget_s of CPU work; returns (TFLOP/s, rows, seconds, threads, rows_out)."""
+    import numpy as np
+    import oracle
+    M, K = A.shape
+    N = B.shape[1]
+    threads = oracle.host_threads()
+    rows_done, spent, outs = 0, 0.0, []
+    while rows_done < M and spent < budget_s:
+        rows = np.arange(rows_done, min(M, rows_done + 16), dtype=np.int64)
+        t0 = time.perf_counter()
+        outs.append(oracle.gemm_bias_relu_rows(A, B, bias, rows, threads=threads))
+        spent += time.perf_counter() - t0
+        rows_done += rows.size
+    flops = 2.0 * rows_done * N * K
+    return flops / spent / 1e12, rows_done, spent, threads, np.concatenate(outs, axis=0)
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import warp_specialized_gemm_amd as wsg
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w, A, B, bias = make_gemm_inputs(args.workload)
+    M, N, K = w["M"], w["N"], w["K"]
+    dtype = w["dtype"]
+    stages = args.stages or w["stages"]
+    config = None
+    if any(v for v in (args.bm, args.bn, args.bk, args.producers, args.consumers)):
+        config = dict(BM=args.bm or 0, BN=args.bn or 0, BK=args.bk or 0,
+                      producer_waves=args.producers or 0, consumer_waves=args.consumers or 0)
+    resolved = wsg.resolve_config(wsg.WSG_FP32 if dtype == "fp32" else wsg.WSG_BF16, M, N, K, stages, config)
+    log("gemm workload %d %s: %s stages=%d" % (args.workload, w["name"], resolved, stages))
+
+    tdt = torch.float32 if dtype == "fp32" else torch.int16
+    dA = torch.from_numpy(A.view(np.int16) if dtype != "fp32" else A).to(dev)
+    dB = torch.from_numpy(B.view(np.int16) if dtype != "fp32" else B).to(dev)
+    dbias = torch.from_numpy(bias.view(np.int16) if dtype != "fp32" else bias).to(dev)
+    assert dA.dtype == tdt
+    dC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    gemm = gemm_launcher(wsg, w, dA, dB, dbias, dC, stages, config)
+
+    cw = synth.WORKLOADS[2]
+    copy_src = None
+    if not args.no_copy:
+        nel = cw["bytes"] // 4
+        copy_src = torch.from_numpy(synth.uniform_pm1(synth.seed_for(2, "src"), nel)).to(dev)
+        copy_dst = torch.empty_like(copy_src)
+        copy_cfg = dict(copy_tile_bytes=cw["tile_bytes"])
+        copy = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=cw["stages"], config=copy_cfg)  # noqa: E731
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        gemm()
+        if copy_src is not None:
+            copy()
+    wsg.check_device_status()
+
+    log("timing %d steps" % args.steps)
+    g_wall, g_kern, g_min = time_region(torch, gemm, args.steps)
+    wsg.check_device_status()
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops * args.steps / g_wall / 1e12
+    result = {
+        "metric": "GEMM+bias+ReLU TFLOP/s (% MFMA peak); LDS-staged copy HBM GB/s",
+        "value": round(gemm_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if dtype == "fp32" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w["name"] + (" + " + cw["name"] if copy_src is not None else ""),
+            "M": M, "N": N, "K": K, "stages": stages,
+            "tile": [resolved["BM"], resolved["BN"], resolved["BK"]],
+            "producer_waves": resolved["producer_waves"], "consumer_waves": resolved["consumer_waves"],
+            "input": "uniform[-1,1) splitmix64" if dtype == "fp32" else "N(0,1)*0.1 rounded to bf16",
+        },
+    }
+    peak = PEAK_TFLOPS[dtype]
+    achieved = flops / g_kern / 1e12
+    traffic = measured_traffic("gemm_w%d_%s" % (args.workload, "x".join(str(resolved[k]) for k in
+                                                                         ("BM", "BN", "BK"))), "gemm")
+    result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                          "frac": round(achieved / peak, 4), "traffic": traffic,
+                          "kernel_ms": round(g_kern * 1e3, 4), "kernel_ms_min": round(g_min * 1e3, 4)}
+    step_s = g_wall / args.steps
+
+    if copy_src is not None:
+        c_wall, c_kern, c_min = time_region(torch, copy, args.steps)
+        wsg.check_device_status()
+        nbytes = cw["bytes"]
+        moved = 2.0 * nbytes
+        result["copy"] = {"value": round(moved * args.steps / c_wall / 1e9, 1), "unit": "GB/s",
+                          "bytes": nbytes, "tile_bytes": cw["tile_bytes"], "stages": cw["stages"]}
+        c_ach = moved / c_kern / 1e9
+        result["copy_roofline"] = {"bound": "hbm", "achieved": round(c_ach, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(c_ach / PEAK_HBM_GBS, 4),
+                                   "traffic": measured_traffic("copy_1GiB_64KiB", "copy"),
+                                   "kernel_ms": round(c_kern * 1e3, 4), "kernel_ms_min": round(c_min * 1e3, 4)}
+        step_s += c_wall / args.steps
+        if args.check:
+            eq = torch.equal(copy_dst, copy_src)
+            result["copy"]["bit_exact_vs_source"] = bool(eq)
+    result["ms_per_step"] = round(step_s * 1e3, 4)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, about %.0f s)" % args.cpu_budget)
+        tf, rows, secs, threads, ref = cpu_baseline_gemm(A, B, bias, args.cpu_budget)
+        result["cpu_baseline"] = {"value": round(tf, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                                  "sample": "first %d rows of the %dx%dx%d GEMM (%d x %d x %d), %.1f s"
+                                            % (rows, M, N, K, rows, N, K, secs)}
+        got = dC[:rows].cpu().numpy()
+        s = oracle.compare(got, ref)
+        result["parity"] = {"rows_checked": rows, "max_abs": s["max_abs"], "rel_fro": s["rel_fro"],
+                            "pass": bool(oracle.within_tolerance(s, dtype))}
+    return result
+
+
+def sweep(args):
+    """cfg: S in 2,3,4 x 1 or 2 producer waves on the 4096^3 fp32 GEMM."""
+    import copy as _copy
+    out = []
+    for producers in (1, 2):
+        for stages in (2, 3, 4):
+            a = _copy.copy(args)
+            a.stages, a.producers, a.no_copy, a.no_cpu_baseline = stages, producers, True, True
+            a.bm, a.bn, a.bk, a.consumers = a.bm or 128, a.bn or 128, a.bk or 16, a.consumers or 4
+            try:
+                r = run(a)
+                line = {"stages": stages, "producer_waves": producers, "tile": r["config"]["tile"],
+                        "consumer_waves": r["config"]["consumer_waves"], "tflops": r["value"],
+                        "kernel_tflops": r["roofline"]["achieved"], "frac": r["roofline"]["frac"]}
+            except Exception as e:  # an unsupported point is reported, not fatal
+                line = {"stages": stages, "producer_waves": producers, "error": str(e)}
+            print(json.dumps(line), flush=True)
+            out.append(line)
+    return out
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=3, choices=[1, 3, 4, 5])
+    p.add_argument("--stages", type=int, default=0)
+    p.add_argument("--bm", type=int, default=0)
+    p.add_argument("--bn", type=int, default=0)
+    p.add_argument("--bk", type=int, default=0)
+    p.add_argument("--producers", type=int, default=0)
+    p.add_argument("--consumers", type=int, default=0)
+    p.add_argument("--no-copy", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    p.add_argument("--check", action="store_true", help="also compare the copy's output on the GPU")
+    p.add_argument("--sweep", action="store_true")
+    args = p.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run the same "
+              "kernels on its own share of output tiles or bytes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
+    print(json.dumps(run(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -133,6 +133,13 @@ def test_variants_and_stages_integer_bit_exact(gpu, config, stages):
     # several tiles in both directions, a ragged edge, and enough k-tiles to lap the ring
     M, N, K = 300, 520, 16 * 13 + 4
     A, B, bias = int_case(1000 + stages, M, N, K)
+    lds = 256 + stages * (config["BM"] * config["BK"] + config["BK"] * config["BN"]) * 4
+    if lds > 163840:
+        # a ring that does not fit in LDS is refused, not launched
+        with pytest.raises(gpu.WsgError) as e:
+            run_gemm(gpu, A, B, bias, stages=stages, config=config)
+        assert e.value.code == gpu.WSG_EUNSUPPORTED
+        return
     C = run_gemm(gpu, A, B, bias, stages=stages, config=config)
     assert np.array_equal(C.astype(np.float64), oracle.gemm_bias_relu(A, B, bias))
 
