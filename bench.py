@@ -159,8 +159,10 @@ def run(args):
         nel = cw["bytes"] // 4
         copy_src = torch.from_numpy(synth.uniform_pm1(synth.seed_for(2, "src"), nel)).to(dev)
         copy_dst = torch.empty_like(copy_src)
-        copy_cfg = dict(copy_tile_bytes=cw["tile_bytes"])
-        copy = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=cw["stages"], config=copy_cfg)  # noqa: E731
+        copy_cfg = dict(copy_tile_bytes=args.copy_tile or cw["tile_bytes"], producer_waves=args.copy_producers,
+                        consumer_waves=args.copy_consumers)
+        copy_stages = args.copy_stages or cw["stages"]
+        copy = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=copy_stages, config=copy_cfg)  # noqa: E731
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -210,7 +212,8 @@ def run(args):
         nbytes = cw["bytes"]
         moved = 2.0 * nbytes
         result["copy"] = {"value": round(moved * args.steps / c_wall / 1e9, 1), "unit": "GB/s",
-                          "bytes": nbytes, "tile_bytes": cw["tile_bytes"], "stages": cw["stages"]}
+                          "bytes": nbytes, "tile_bytes": copy_cfg["copy_tile_bytes"], "stages": copy_stages,
+                          "producer_waves": args.copy_producers or None, "consumer_waves": args.copy_consumers or None}
         c_ach = moved / c_kern / 1e9
         result["copy_roofline"] = {"bound": "hbm", "achieved": round(c_ach, 1), "peak": PEAK_HBM_GBS,
                                    "unit": "GB/s", "frac": round(c_ach / PEAK_HBM_GBS, 4),
@@ -269,6 +272,10 @@ def main():
     p.add_argument("--producers", type=int, default=0)
     p.add_argument("--consumers", type=int, default=0)
     p.add_argument("--no-copy", action="store_true")
+    p.add_argument("--copy-tile", type=int, default=0, help="staged copy: bytes per ring slot")
+    p.add_argument("--copy-stages", type=int, default=0)
+    p.add_argument("--copy-producers", type=int, default=0)
+    p.add_argument("--copy-consumers", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     p.add_argument("--check", action="store_true", help="also compare the copy's output on the GPU")

@@ -10,24 +10,32 @@
 // Slot = t mod S, full-wait parity = (t / S) & 1, empty-wait parity =
 // ((t / S) & 1) ^ 1 (ring.hpp).
 //
-// Producers (two builds):
-//   DMA      16-byte LDS-DMA loads through buffer resources (the analogue of
-//            an asynchronous bulk copy: no VGPRs, completion by vmcnt). Chunks
-//            past M, N or K get an out-of-range offset, which loads zeros, so
-//            consumers never mask. Up to S - 1 tiles stay in flight. Needs
-//            16-byte aligned rows (K, N multiples of 4 for fp32).
-//   general  per-element masked loads into VGPRs, then 16-byte LDS writes in
-//            the same slot layout; any shape and 4-byte alignment.
+// Producers
+//   A (both dtypes) and B (fp32) go global -> LDS by 16-byte LDS-DMA loads
+//   through buffer resources (no VGPRs; completion by vmcnt), the analogue of
+//   an asynchronous bulk copy. Chunks past M, N or K get an out-of-range
+//   offset, which loads zeros, so consumers never mask. Up to S - 1 tiles stay
+//   in flight. This needs 16-byte aligned rows; other shapes use a
+//   register-staged producer with per-element masks and the same slot layout.
+//   B (bf16) must arrive k-contiguous per column for the bf16 MFMA, so the
+//   producer loads 8x8 blocks of B into VGPRs, transposes them with byte
+//   permutes and writes B^T into the slot, one tile ahead of the one it
+//   publishes.
 //
-// Slot layout (fp32): A as BM rows of BK floats, 16-byte chunks XOR-swizzled
-// within a row so that 8 consecutive rows read the same chunk index from
-// distinct banks; B as BK rows of BN floats.
+// Slot layout: A as BM rows of BK elements, B^T (bf16) as BN rows of BK
+// elements, both in 16-byte chunks XOR-swizzled within a row so that
+// consecutive rows reading the same chunk index hit distinct banks; B (fp32)
+// as BK rows of BN floats, chunks swizzled by k.
 //
-// Consumers run v_mfma_f32_32x32x2_f32. Over one 16-deep k group a lane of
-// half h (lanes 32h..32h+31) supplies k = 16g + 8h + j at step j = 0..7, so
-// its eight A values are two consecutive 16-byte chunks of one row; B values
-// are single floats of one column. The slot is released as soon as the
-// fragments are in registers, before the MFMAs run.
+// Consumers
+//   fp32: v_mfma_f32_16x16x4_f32. Over a 16-deep k group, lane group q
+//   (lanes 16q..16q+15) supplies k = 16g + 4q + j at step j = 0..3, so each
+//   lane's four A values are one 16-byte chunk of its row.
+//   bf16: v_mfma_f32_32x32x16_bf16; lane half h supplies k = 16g + 8h + e,
+//   one 16-byte chunk of A and one of B^T.
+//   The fragments of the next k group are read while the MFMAs of the current
+//   one run, and a slot is released as soon as its last group is in
+//   registers.
 #include "internal.hpp"
 #include "ring.hpp"
 
@@ -35,6 +43,8 @@ namespace wsg {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
     const unsigned char *A;
@@ -70,26 +80,215 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 
 __device__ __forceinline__ float relu_f32(float v) { return (v > 0.0f || v != v) ? v : 0.0f; }
 
+// XOR applied to the chunk index of row m (QPR chunks of 16 bytes per row)
 template <int QPR>
-__device__ __forceinline__ int a_swizzle(int m) {
-    // chunk index XOR so that 8 consecutive rows hit 8 distinct 16-byte bank groups
+__device__ __forceinline__ int row_swizzle(int m) {
     if constexpr (QPR == 4) return (m >> 1) & 3;
     else return m & 7;
 }
 
+// XOR applied to the chunk index of row k of an fp32 B slot (BN/4 >= 16 chunks)
+__device__ __forceinline__ int bk_swizzle(int k) { return ((k >> 2) & 3) << 2; }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ----------------------------------------------------------------------------
+// A by LDS-DMA: BM rows x BK elements of ES bytes, QPR chunks per row.
+// ----------------------------------------------------------------------------
+template <int BM, int BK, int ES, int P>
+struct ADma {
+    static constexpr int EPC = 16 / ES;  // elements per chunk
+    static constexpr int QPR = BK / EPC;
+    static constexpr int CHUNKS = BM * QPR;
+    static constexpr int NL = CHUNKS / (64 * P);
+    static_assert(CHUNKS % (64 * P) == 0, "A chunks split evenly over producer waves");
+    uint32_t off[NL];
+    int kq[NL];
+    bool ok[NL];
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t K, int rows_valid) {
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            const int p = (r * P + wave) * 64 + lane;
+            const int m = p / QPR;
+            const int q = (p % QPR) ^ row_swizzle<QPR>(m);
+            off[r] = (uint32_t)m * (uint32_t)K * ES + (uint32_t)q * 16u;
+            kq[r] = q * EPC;
+            ok[r] = m < rows_valid;
+        }
+    }
+    __device__ __forceinline__ void issue(unsigned char *slot, int wave, const unsigned char *A_rows, int rows_valid,
+                                          int64_t K, int64_t k0) const {
+        const int64_t rec = ((int64_t)rows_valid * K - k0) * ES;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(A_rows + (size_t)k0 * ES, (uint32_t)min(rec, (int64_t)0x7FFFFFFF));
+#pragma unroll
+        for (int r = 0; r < NL; ++r)
+            lds_dma16(rs, slot + (r * P + wave) * 1024, (ok[r] && k0 + kq[r] < K) ? off[r] : kOobOffset);
+    }
+};
+
+// ----------------------------------------------------------------------------
+// fp32 B by LDS-DMA: BK rows x BN floats, chunks swizzled by k.
+// ----------------------------------------------------------------------------
+template <int BN, int BK, int P>
+struct BDmaF32 {
+    static constexpr int CPR = BN / 4;
+    static constexpr int CHUNKS = BK * CPR;
+    static constexpr int NL = CHUNKS / (64 * P);
+    static_assert(CHUNKS % (64 * P) == 0 && CPR >= 16, "B chunks");
+    uint32_t off[NL];
+    int kk[NL];
+    bool ok[NL];
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t N, int64_t n0) {
+#pragma unroll
+        for (int r = 0; r < NL; ++r) {
+            const int p = (r * P + wave) * 64 + lane;
+            const int k = p / CPR;
+            const int c = (p % CPR) ^ bk_swizzle(k);
+            off[r] = (uint32_t)k * (uint32_t)N * 4u + (uint32_t)c * 16u;
+            kk[r] = k;
+            ok[r] = n0 + 4 * c < N;
+        }
+    }
+    __device__ __forceinline__ void issue(unsigned char *slotB, int wave, const unsigned char *B, int64_t N, int64_t K,
+                                          int64_t n0, int64_t k0) const {
+        const int64_t rec = (K * N - k0 * N - n0) * 4;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(B + (size_t)(k0 * N + n0) * 4u, (uint32_t)min(rec, (int64_t)0x7FFFFFFF));
+#pragma unroll
+        for (int r = 0; r < NL; ++r)
+            lds_dma16(rs, slotB + (r * P + wave) * 1024, (ok[r] && k0 + kk[r] < K) ? off[r] : kOobOffset);
+    }
+};
+
+// ----------------------------------------------------------------------------
+// Register-staged loads with per-element masks, same slot layouts.
+// ----------------------------------------------------------------------------
+template <int BM, int BK, int ES, int P>
+__device__ __forceinline__ void a_general(unsigned char *slotA, int wave, int lane, const unsigned char *A, int64_t m0,
+                                          int rows_valid, int64_t K, int64_t k0) {
+    constexpr int EPC = 16 / ES, QPR = BK / EPC, NL = BM * QPR / (64 * P);
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+        const int p = (r * P + wave) * 64 + lane;
+        const int m = p / QPR;
+        const int q = (p % QPR) ^ row_swizzle<QPR>(m);
+        u32x4 v;
+        if constexpr (ES == 4) {
+            const float *Af = reinterpret_cast<const float *>(A);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t k = k0 + 4 * q + e;
+                v[e] = (m < rows_valid && k < K) ? __float_as_uint(Af[(m0 + m) * K + k]) : 0u;
+            }
+        } else {
+            const uint16_t *Ah = reinterpret_cast<const uint16_t *>(A);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t k = k0 + 8 * q + 2 * e;
+                const uint32_t lo = (m < rows_valid && k < K) ? Ah[(m0 + m) * K + k] : 0u;
+                const uint32_t hi = (m < rows_valid && k + 1 < K) ? Ah[(m0 + m) * K + k + 1] : 0u;
+                v[e] = lo | (hi << 16);
+            }
+        }
+        *reinterpret_cast<u32x4 *>(slotA + (size_t)p * 16u) = v;
+    }
+}
+
+template <int BN, int BK, int P>
+__device__ __forceinline__ void b_general_f32(unsigned char *slotB, int wave, int lane, const float *B, int64_t N,
+                                              int64_t K, int64_t n0, int64_t k0) {
+    constexpr int CPR = BN / 4, NL = BK * CPR / (64 * P);
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+        const int p = (r * P + wave) * 64 + lane;
+        const int k = p / CPR;
+        const int c = (p % CPR) ^ bk_swizzle(k);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t n = n0 + 4 * c + e;
+            v[e] = (k0 + k < K && n < N) ? B[(k0 + k) * N + n] : 0.0f;
+        }
+        *reinterpret_cast<f32x4 *>(slotB + (size_t)p * 16u) = v;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// bf16 B: 8x8 blocks loaded into VGPRs, transposed, written as B^T rows.
+// ----------------------------------------------------------------------------
+template <int BN, int BK, int P>
+struct BTransBf16 {
+    static constexpr int NBN = BN / 8, NBK = BK / 8;
+    static constexpr int NBLK = NBN * NBK;
+    static constexpr int NBL = (NBLK + 64 * P - 1) / (64 * P);  // blocks per lane (the last may be idle)
+    static constexpr int QPR = BK / 8;
+    u32x4 v[NBL][8];
+
+    // fast: every row chunk is 16-byte aligned (N % 8 == 0 and B 16-byte aligned)
+    template <bool FAST>
+    __device__ __forceinline__ void load(int wave, int lane, const uint16_t *B, int64_t N, int64_t K, int64_t n0,
+                                         int64_t k0) {
+#pragma unroll
+        for (int b = 0; b < NBL; ++b) {
+            const int blk = (b * P + wave) * 64 + lane;
+            const int kb = blk / NBN, nb = blk % NBN;
+            const int64_t n = blk < NBLK ? n0 + 8 * nb : N;  // idle lanes load nothing
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int64_t k = k0 + 8 * kb + r;
+                if (FAST) {
+                    if (k < K && n < N)
+                        v[b][r] = *reinterpret_cast<const u32x4 *>(B + k * N + n);
+                    else
+                        v[b][r] = u32x4{0u, 0u, 0u, 0u};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = (k < K && n + 2 * e < N) ? B[k * N + n + 2 * e] : 0u;
+                        const uint32_t hi = (k < K && n + 2 * e + 1 < N) ? B[k * N + n + 2 * e + 1] : 0u;
+                        v[b][r][e] = lo | (hi << 16);
+                    }
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(unsigned char *slotB, int wave, int lane) const {
+#pragma unroll
+        for (int b = 0; b < NBL; ++b) {
+            const int blk = (b * P + wave) * 64 + lane;
+            const int kb = blk / NBN, nb = blk % NBN;
+            if (blk >= NBLK) continue;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                // column c of the block: k pairs (2d, 2d+1) of element c
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(v[b][2 * d + 1][c >> 1], v[b][2 * d][c >> 1], sel);
+                const int nrow = 8 * nb + c;
+                *reinterpret_cast<u32x4 *>(slotB + nrow * QPR * 16 + ((kb ^ row_swizzle<QPR>(nrow)) << 4)) = o;
+            }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------
+// fp32 kernel
+// ----------------------------------------------------------------------------
 template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA>
 __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs a) {
     constexpr int NCW = CWM * CWN;
     constexpr int WTM = BM / CWM, WTN = BN / CWN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int QPR = BK / 4;
     constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4, SLOT = A_BYTES + B_BYTES;
-    constexpr int A_CHUNKS = BM * QPR, B_CHUNKS = BK * BN / 4;
-    constexpr int NLA = A_CHUNKS / (64 * P), NLB = B_CHUNKS / (64 * P);
-    constexpr int NL = NLA + NLB;
     constexpr int KG = BK / 16;
-    static_assert(BK % 16 == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
-    static_assert(A_CHUNKS % (64 * P) == 0 && B_CHUNKS % (64 * P) == 0, "chunks split evenly over producer waves");
+    using AD = ADma<BM, BK, 4, P>;
+    using BD = BDmaF32<BN, BK, P>;
+    constexpr int NL = AD::NL + BD::NL;
+    static_assert(BK % 16 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
     static_assert(NL <= 63, "one tile's loads must fit vmcnt");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -111,55 +310,21 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     if (wave < P) {
         // ================= producer =================
         const int rows_valid = (int)min((int64_t)BM, M - m0);
+        const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * 4u;
+        int s = 0;
+        uint32_t lap = 0;
         if constexpr (DMA) {
-            uint32_t a_off[NLA];
-            int a_q[NLA];
-            bool a_ok[NLA];
-#pragma unroll
-            for (int r = 0; r < NLA; ++r) {
-                const int p = (r * P + wave) * 64 + lane;
-                const int m = p / QPR;
-                const int q = (p % QPR) ^ a_swizzle<QPR>(m);
-                a_off[r] = (uint32_t)m * (uint32_t)K * 4u + (uint32_t)q * 16u;
-                a_q[r] = q;
-                a_ok[r] = m < rows_valid;
-            }
-            uint32_t b_off[NLB];
-            int b_k[NLB];
-            bool b_ok[NLB];
-#pragma unroll
-            for (int r = 0; r < NLB; ++r) {
-                const int p = (r * P + wave) * 64 + lane;
-                const int k = p / (BN / 4);
-                const int c = p % (BN / 4);
-                b_off[r] = (uint32_t)k * (uint32_t)N * 4u + (uint32_t)c * 16u;
-                b_k[r] = k;
-                b_ok[r] = n0 + 4 * c < N;
-            }
-            const unsigned char *Abase = a.A + (size_t)m0 * (size_t)K * 4u;
+            AD ad;
+            BD bd;
+            ad.init(wave, lane, K, rows_valid);
+            bd.init(wave, lane, N, n0);
             const int D = min(S - 1, 63 / NL);
-            int s = 0;
-            uint32_t lap = 0;
             for (int t = 0; t < T; ++t) {
                 if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
                 const int64_t k0 = (int64_t)t * BK;
                 unsigned char *slot = ring + (size_t)s * SLOT;
-                const int64_t a_rec = ((int64_t)rows_valid * K - k0) * 4;
-                const __amdgpu_buffer_rsrc_t ra =
-                    make_rsrc(Abase + (size_t)k0 * 4u, (uint32_t)min(a_rec, (int64_t)0x7FFFFFFF));
-#pragma unroll
-                for (int r = 0; r < NLA; ++r) {
-                    const bool ok = a_ok[r] && (k0 + 4 * a_q[r] < K);
-                    lds_dma16(ra, slot + (r * P + wave) * 1024, ok ? a_off[r] : kOobOffset);
-                }
-                const int64_t b_rec = (K * N - k0 * N - n0) * 4;
-                const __amdgpu_buffer_rsrc_t rb =
-                    make_rsrc(a.B + (size_t)(k0 * N + n0) * 4u, (uint32_t)min(b_rec, (int64_t)0x7FFFFFFF));
-#pragma unroll
-                for (int r = 0; r < NLB; ++r) {
-                    const bool ok = b_ok[r] && (k0 + b_k[r] < K);
-                    lds_dma16(rb, slot + A_BYTES + (r * P + wave) * 1024, ok ? b_off[r] : kOobOffset);
-                }
+                ad.issue(slot, wave, A_rows, rows_valid, K, k0);
+                bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
                 if (t >= D) {
                     wait_vmcnt_dyn(D * NL);
                     flag_arrive(full_flag(fb, (t - D) % S), P);
@@ -174,40 +339,13 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
                 flag_arrive(full_flag(fb, t % S), P);
             }
         } else {
-            const float *A = reinterpret_cast<const float *>(a.A);
-            const float *B = reinterpret_cast<const float *>(a.B);
-            int s = 0;
-            uint32_t lap = 0;
             for (int t = 0; t < T; ++t) {
                 if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
                 const int64_t k0 = (int64_t)t * BK;
                 unsigned char *slot = ring + (size_t)s * SLOT;
-#pragma unroll
-                for (int r = 0; r < NLA; ++r) {
-                    const int p = (r * P + wave) * 64 + lane;
-                    const int m = p / QPR;
-                    const int q = (p % QPR) ^ a_swizzle<QPR>(m);
-                    f32x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t k = k0 + 4 * q + e;
-                        v[e] = (m < rows_valid && k < K) ? A[(m0 + m) * K + k] : 0.0f;
-                    }
-                    *reinterpret_cast<f32x4 *>(slot + (size_t)p * 16u) = v;
-                }
-#pragma unroll
-                for (int r = 0; r < NLB; ++r) {
-                    const int p = (r * P + wave) * 64 + lane;
-                    const int k = p / (BN / 4);
-                    const int c = p % (BN / 4);
-                    f32x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t n = n0 + 4 * c + e;
-                        v[e] = (k0 + k < K && n < N) ? B[(k0 + k) * N + n] : 0.0f;
-                    }
-                    *reinterpret_cast<f32x4 *>(slot + A_BYTES + (size_t)p * 16u) = v;
-                }
+                a_general<BM, BK, 4, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
+                b_general_f32<BN, BK, P>(slot + A_BYTES, wave, lane, reinterpret_cast<const float *>(a.B), N, K, n0,
+                                         k0);
                 wait_lgkm0();
                 flag_arrive(full_flag(fb, s), P);
                 if (++s == S) {
@@ -216,6 +354,210 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
                 }
             }
         }
+        return;
+    }
+
+    // ================= consumer =================
+    const int cw = wave - P;
+    const int wr = cw / CWN, wc = cw % CWN;
+    const int li = lane & 15, q = lane >> 4;
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int a_off[FM], a_swz[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = wr * WTM + 16 * i + li;
+        a_off[i] = row * QPR * 16;
+        a_swz[i] = row_swizzle<QPR>(row);
+    }
+    int b_chunk[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_chunk[j] = (wc * WTN + 16 * j + li) >> 2;
+    const int b_sub = (li & 3) * 4;
+
+    struct Frag {
+        f32x4 a[FM];
+        float b[FN][4];
+    };
+    auto read = [&](Frag &f, const unsigned char *slot, int g) {
+        const unsigned char *slotB = slot + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = *reinterpret_cast<const f32x4 *>(slot + a_off[i] + (((4 * g + q) ^ a_swz[i]) << 4));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int k = 16 * g + 4 * q + jj;
+            const unsigned char *row = slotB + k * BN * 4 + b_sub;
+            const int sw = bk_swizzle(k);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) f.b[j][jj] = *reinterpret_cast<const float *>(row + ((b_chunk[j] ^ sw) << 4));
+        }
+    };
+    auto mma = [&](const Frag &f) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[i][jj], f.b[j][jj], acc[i][j], 0, 0, 0);
+    };
+
+    // Reads run one k group ahead of the MFMAs.
+    const int U = T * KG;
+    Frag f0, f1;
+    int rs = 0, rg = 0;       // slot and group of the next read
+    uint32_t rlap = 0;
+    int cs = 0;               // slot being consumed
+    bool alive = true;
+    if (U > 0) {
+        alive = flag_wait(full_flag(fb, 0), 0u, a.status, kStatusGemm);
+        if (alive) read(f0, ring, 0);
+    }
+    auto step = [&](int u, Frag &cur, Frag &nxt) {
+        wait_lgkm0();  // the reads of group u are in registers
+        const int g = u % KG;
+        if (g == KG - 1) {
+            flag_arrive(empty_flag(fb, cs), NCW);
+            if (++cs == S) cs = 0;
+        }
+        if (u + 1 < U) {
+            if (++rg == KG) {
+                rg = 0;
+                if (++rs == S) {
+                    rs = 0;
+                    ++rlap;
+                }
+                if (!flag_wait(full_flag(fb, rs), rlap & 1u, a.status, kStatusGemm)) {
+                    alive = false;
+                    return;
+                }
+            }
+            read(nxt, ring + (size_t)rs * SLOT, rg);
+        }
+        mma(cur);
+    };
+    for (int u = 0; alive && u < U; u += 2) {
+        step(u, f0, f1);
+        if (alive && u + 1 < U) step(u + 1, f1, f0);
+    }
+    if (!alive) return;
+
+    // epilogue: C = relu(acc + bias[n]); lane (li, q) holds column li and rows
+    // 4q + r of each 16x16 block
+    const float *bias = reinterpret_cast<const float *>(a.bias) + n0;
+    float *ctile = a.C + m0 * N + n0;
+    const int rbase = wr * WTM + 4 * q, cbase = wc * WTN + li;
+    const int rows_valid = (int)min((int64_t)BM, M - m0), cols_valid = (int)min((int64_t)BN, N - n0);
+    if (rows_valid == BM && cols_valid == BN) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = cbase + 16 * j;
+            const float bv = bias[col];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ctile[(int64_t)(rbase + 16 * i + r) * N + col] = relu_f32(acc[i][j][r] + bv);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = cbase + 16 * j;
+            if (col >= cols_valid) continue;
+            const float bv = bias[col];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rbase + 16 * i + r;
+                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv);
+                }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// bf16 kernel
+// ----------------------------------------------------------------------------
+template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA>
+__global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArgs a) {
+    constexpr int NCW = CWM * CWN;
+    constexpr int WTM = BM / CWM, WTN = BN / CWN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int QPR = BK / 8;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, SLOT = A_BYTES + B_BYTES;
+    constexpr int KG = BK / 16;
+    using AD = ADma<BM, BK, 2, P>;
+    using BT = BTransBf16<BN, BK, P>;
+    static_assert(BK % 16 == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *ring = lds + kFlagBytes;
+    const uint32_t fb = lds_addr(lds);
+    const int wave = wave_id();
+    const int lane = lane_id();
+
+    if (threadIdx.x < kFlagBytes / 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0u;
+    __syncthreads();  // the only workgroup barrier
+
+    int tm, tn;
+    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int T = (int)((K + BK - 1) / BK);
+    const int S = a.S;
+
+    if (wave < P) {
+        // ================= producer =================
+        // Tile t's loads are issued right after tile t - 1 is transposed and
+        // published; they land while the producer waits for the next free
+        // slot, so with S > 1 one tile of global latency hides behind that
+        // wait. (With S = 1 the next fill needs this tile consumed first, so
+        // each tile is published before the loop moves on.)
+        const int rows_valid = (int)min((int64_t)BM, M - m0);
+        const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * 2u;
+        const uint16_t *B = reinterpret_cast<const uint16_t *>(a.B);
+        AD ad;
+        if constexpr (DMA) ad.init(wave, lane, K, rows_valid);
+        BT bt;
+        auto issue = [&](int t, int s) {
+            const int64_t k0 = (int64_t)t * BK;
+            unsigned char *slot = ring + (size_t)s * SLOT;
+            if constexpr (DMA) {
+                ad.issue(slot, wave, A_rows, rows_valid, K, k0);
+                bt.template load<true>(wave, lane, B, N, K, n0, k0);
+            } else {
+                a_general<BM, BK, 2, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
+                bt.template load<false>(wave, lane, B, N, K, n0, k0);
+            }
+        };
+        auto publish = [&](int s) {
+            wait_vmcnt<0>();  // only this tile's loads are outstanding
+            bt.store(ring + (size_t)s * SLOT + A_BYTES, wave, lane);
+            wait_lgkm0();
+            flag_arrive(full_flag(fb, s), P);
+        };
+        const bool ahead = S > 1;
+        int s = 0;
+        uint32_t lap = 0;
+        int ps = 0;  // slot of the tile awaiting publication
+        for (int t = 0; t < T; ++t) {
+            if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
+            if (ahead && t > 0) publish(ps);
+            issue(t, s);
+            if (!ahead) publish(s);
+            ps = s;
+            if (++s == S) {
+                s = 0;
+                ++lap;
+            }
+        }
+        if (ahead && T > 0) publish(ps);
         return;
     }
 
@@ -231,70 +573,108 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    int a_row_off[FM], a_swz[FM];
+    int a_off[FM], a_swz[FM], b_off[FN], b_swz[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int row = wr * WTM + 32 * i + li;
-        a_row_off[i] = row * QPR * 16;
-        a_swz[i] = a_swizzle<QPR>(row);
+        a_off[i] = row * QPR * 16;
+        a_swz[i] = row_swizzle<QPR>(row);
     }
-    int b_col[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b_col[j] = wc * WTN + 32 * j + li;
-
-    int s = 0;
-    uint32_t lap = 0;
-    for (int t = 0; t < T; ++t) {
-        if (!flag_wait(full_flag(fb, s), lap & 1u, a.status, kStatusGemm)) return;
-        const unsigned char *slotA = ring + (size_t)s * SLOT;
-        const float *slotB = reinterpret_cast<const float *>(slotA + A_BYTES);
-        f32x4 af[KG][FM][2];
-        float bf[KG][FN][8];
-#pragma unroll
-        for (int g = 0; g < KG; ++g) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int q0 = 4 * g + 2 * h;
-                af[g][i][0] = *reinterpret_cast<const f32x4 *>(slotA + a_row_off[i] + ((q0 ^ a_swz[i]) << 4));
-                af[g][i][1] = *reinterpret_cast<const f32x4 *>(slotA + a_row_off[i] + (((q0 + 1) ^ a_swz[i]) << 4));
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) bf[g][j][kk] = slotB[(16 * g + 8 * h + kk) * BN + b_col[j]];
-        }
-        wait_lgkm0();
-        flag_arrive(empty_flag(fb, s), NCW);
-#pragma unroll
-        for (int g = 0; g < KG; ++g)
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[g][i][kk >> 2][kk & 3], bf[g][j][kk],
-                                                                          acc[i][j], 0, 0, 0);
-        if (++s == S) {
-            s = 0;
-            ++lap;
-        }
-    }
-
-    // epilogue: C = relu(acc + bias[n]); lane (li, h) holds column li of each
-    // 32x32 block and rows 8*(r/4) + 4*h + (r%4) of its 16 registers
-    const float *bias = reinterpret_cast<const float *>(a.bias);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int64_t col = n0 + b_col[j];
-        const float bv = col < N ? bias[col] : 0.0f;
+        const int row = wc * WTN + 32 * j + li;
+        b_off[j] = A_BYTES + row * QPR * 16;
+        b_swz[j] = row_swizzle<QPR>(row);
+    }
+    struct Frag {
+        bf16x8 a[FM];
+        bf16x8 b[FN];
+    };
+    auto read = [&](Frag &f, const unsigned char *slot, int g) {
+        const int c = 2 * g + h;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int i = 0; i < FM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(slot + a_off[i] + ((c ^ a_swz[i]) << 4));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wr * WTM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M && col < N) a.C[row * N + col] = relu_f32(acc[i][j][r] + bv);
+        for (int j = 0; j < FN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(slot + b_off[j] + ((c ^ b_swz[j]) << 4));
+    };
+    auto mma = [&](const Frag &f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+
+    const int U = T * KG;
+    Frag f0, f1;
+    int rs = 0, rg = 0;
+    uint32_t rlap = 0;
+    int cs = 0;
+    bool alive = true;
+    if (U > 0) {
+        alive = flag_wait(full_flag(fb, 0), 0u, a.status, kStatusGemm);
+        if (alive) read(f0, ring, 0);
+    }
+    auto step = [&](int u, Frag &cur, Frag &nxt) {
+        wait_lgkm0();
+        const int g = u % KG;
+        if (g == KG - 1) {
+            flag_arrive(empty_flag(fb, cs), NCW);
+            if (++cs == S) cs = 0;
+        }
+        if (u + 1 < U) {
+            if (++rg == KG) {
+                rg = 0;
+                if (++rs == S) {
+                    rs = 0;
+                    ++rlap;
+                }
+                if (!flag_wait(full_flag(fb, rs), rlap & 1u, a.status, kStatusGemm)) {
+                    alive = false;
+                    return;
+                }
             }
+            read(nxt, ring + (size_t)rs * SLOT, rg);
+        }
+        mma(cur);
+    };
+    for (int u = 0; alive && u < U; u += 2) {
+        step(u, f0, f1);
+        if (alive && u + 1 < U) step(u + 1, f1, f0);
+    }
+    if (!alive) return;
+
+    // epilogue: lane (li, h) holds column li of each 32x32 block and rows
+    // 8*(r/4) + 4*h + (r%4) of its 16 registers
+    const uint16_t *bias = reinterpret_cast<const uint16_t *>(a.bias) + n0;
+    float *ctile = a.C + m0 * N + n0;
+    const int rbase = wr * WTM + 4 * h, cbase = wc * WTN + li;
+    const int rows_valid = (int)min((int64_t)BM, M - m0), cols_valid = (int)min((int64_t)BN, N - n0);
+    if (rows_valid == BM && cols_valid == BN) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = cbase + 32 * j;
+            const float bv = bf16_to_f32(bias[col]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    ctile[(int64_t)(rbase + 32 * i + 8 * (r >> 2) + (r & 3)) * N + col] =
+                        relu_f32(acc[i][j][r] + bv);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = cbase + 32 * j;
+            if (col >= cols_valid) continue;
+            const float bv = bf16_to_f32(bias[col]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv);
+                }
         }
     }
 }
@@ -304,12 +684,22 @@ namespace {
 #define WSG_F32(BM, BN, BK, P, CWM, CWN, DMA)                                                              \
     {WSG_FP32, BM, BN, BK, P, CWM, CWN, DMA,                                                               \
      reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA>)}
+#define WSG_BF(BM, BN, BK, P, CWM, CWN, DMA)                                                               \
+    {WSG_BF16, BM, BN, BK, P, CWM, CWN, DMA,                                                               \
+     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA>)}
 
+// First match wins when the caller leaves fields at 0, so each group starts
+// with its default.
 const GemmVariant kGemmVariants[] = {
-    WSG_F32(128, 128, 16, 1, 2, 2, true),  WSG_F32(128, 128, 16, 2, 2, 2, true),
-    WSG_F32(256, 128, 16, 2, 4, 2, true),  WSG_F32(128, 256, 16, 2, 2, 4, true),
-    WSG_F32(128, 128, 32, 2, 2, 2, true),  WSG_F32(64, 64, 16, 1, 2, 2, true),
+    WSG_F32(256, 128, 16, 2, 4, 2, true),  WSG_F32(128, 128, 16, 1, 2, 2, true),
+    WSG_F32(128, 128, 16, 2, 2, 2, true),  WSG_F32(128, 256, 16, 2, 2, 4, true),
+    WSG_F32(128, 128, 32, 2, 2, 2, true),  WSG_F32(256, 128, 32, 2, 4, 2, true),
+    WSG_F32(64, 64, 16, 1, 2, 2, true),    WSG_F32(256, 128, 16, 2, 4, 2, false),
     WSG_F32(128, 128, 16, 1, 2, 2, false), WSG_F32(64, 64, 16, 1, 2, 2, false),
+    WSG_BF(256, 128, 32, 1, 2, 2, true),   WSG_BF(128, 128, 32, 1, 2, 2, true),
+    WSG_BF(256, 128, 64, 2, 2, 2, true),   WSG_BF(64, 64, 32, 1, 2, 2, true),
+    WSG_BF(256, 128, 32, 1, 2, 2, false),  WSG_BF(128, 128, 32, 1, 2, 2, false),
+    WSG_BF(64, 64, 32, 1, 2, 2, false),
 };
 
 }  // namespace
@@ -324,40 +714,40 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
         *err = "stages above the flag area's limit of " + std::to_string(kMaxStages);
         return WSG_EUNSUPPORTED;
     }
-    if (dtype != WSG_FP32) {
-        *err = "dtype not built";
-        return WSG_EUNSUPPORTED;
-    }
-    const int esz = 4;
+    const int esz = dtype == WSG_FP32 ? 4 : 2;
     int BM = cfg && cfg->BM ? cfg->BM : 0, BN = cfg && cfg->BN ? cfg->BN : 0, BK = cfg && cfg->BK ? cfg->BK : 0;
     int P = cfg && cfg->producer_waves ? cfg->producer_waves : 0;
     int CW = cfg && cfg->consumer_waves ? cfg->consumer_waves : 0;
     bool force_general = cfg && (cfg->flags & WSG_FLAG_GENERAL_PRODUCER);
     if (!BM && !BN && !BK) {
         // default tile by problem size: small problems need more workgroups
-        if ((M + 127) / 128 * ((N + 127) / 128) >= (int64_t)dev.cu_count) {
+        const int64_t big = (M + 255) / 256 * ((N + 127) / 128);
+        const int64_t mid = (M + 127) / 128 * ((N + 127) / 128);
+        if (big >= (int64_t)dev.cu_count) {
+            BM = 256;
+            BN = 128;
+        } else if (mid >= (int64_t)dev.cu_count / 2) {
             BM = 128;
             BN = 128;
         } else {
             BM = 64;
             BN = 64;
         }
-        BK = 16;
     }
     // the DMA producer needs 16-byte aligned rows and offsets within 31 bits
-    const bool aligned = (K * esz) % 16 == 0 && (N * esz) % 16 == 0 && ((uintptr_t)A % 16) == 0 &&
+    const int align_elems = 16 / esz;
+    const bool aligned = K % align_elems == 0 && N % align_elems == 0 && ((uintptr_t)A % 16) == 0 &&
                          ((uintptr_t)B % 16) == 0;
     const GemmVariant *pick = nullptr;
     for (int pass = 0; pass < 2 && !pick; ++pass) {
         const bool want_dma = pass == 0;
         if (want_dma && (force_general || !aligned)) continue;
-        if (want_dma && ((int64_t)(BM ? BM : 256) * K * esz >= 0x7FFFFFFF ||
-                         (int64_t)(BK ? BK : 64) * N * esz >= 0x7FFFFFFF))
-            continue;
         for (const GemmVariant &v : kGemmVariants) {
             if (v.dtype != dtype || v.dma != want_dma) continue;
             if ((BM && v.BM != BM) || (BN && v.BN != BN) || (BK && v.BK != BK)) continue;
             if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW)) continue;
+            if (want_dma && ((int64_t)v.BM * K * esz >= 0x7FFFFFFF || (int64_t)v.BK * N * esz >= 0x7FFFFFFF))
+                continue;
             pick = &v;
             break;
         }

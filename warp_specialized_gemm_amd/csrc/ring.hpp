@@ -96,7 +96,14 @@ __device__ __forceinline__ void flag_arrive(uint32_t addr, uint32_t expected) {
     }
 }
 
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// All of this wave's LDS operations done. The builtin (not inline assembly)
+// lets the compiler's own wait insertion see it, so later uses of registers
+// loaded before it need no further wait.
+__device__ __forceinline__ void wait_lgkm0() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: lgkmcnt(0), vmcnt and expcnt unconstrained
+    asm volatile("" ::: "memory");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
