@@ -160,7 +160,7 @@ def run(args):
         copy_src = torch.from_numpy(synth.uniform_pm1(synth.seed_for(2, "src"), nel)).to(dev)
         copy_dst = torch.empty_like(copy_src)
         copy_cfg = dict(copy_tile_bytes=args.copy_tile or cw["tile_bytes"], producer_waves=args.copy_producers,
-                        consumer_waves=args.copy_consumers)
+                        consumer_waves=args.copy_consumers, flags=0 if args.copy_cached else wsg.WSG_FLAG_NONTEMPORAL)
         copy_stages = args.copy_stages or cw["stages"]
         copy = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=copy_stages, config=copy_cfg)  # noqa: E731
 
@@ -213,7 +213,8 @@ def run(args):
         moved = 2.0 * nbytes
         result["copy"] = {"value": round(moved * args.steps / c_wall / 1e9, 1), "unit": "GB/s",
                           "bytes": nbytes, "tile_bytes": copy_cfg["copy_tile_bytes"], "stages": copy_stages,
-                          "producer_waves": args.copy_producers or None, "consumer_waves": args.copy_consumers or None}
+                          "producer_waves": args.copy_producers or None, "consumer_waves": args.copy_consumers or None,
+                          "nontemporal": not args.copy_cached}
         c_ach = moved / c_kern / 1e9
         result["copy_roofline"] = {"bound": "hbm", "achieved": round(c_ach, 1), "peak": PEAK_HBM_GBS,
                                    "unit": "GB/s", "frac": round(c_ach / PEAK_HBM_GBS, 4),
@@ -224,6 +225,13 @@ def run(args):
             eq = torch.equal(copy_dst, copy_src)
             result["copy"]["bit_exact_vs_source"] = bool(eq)
     result["ms_per_step"] = round(step_s * 1e3, 4)
+
+    if args.calibrate_copy and copy_src is not None:
+        # a plain device copy of known size (torch's copy kernel), outside the
+        # timed regions, for scaling the HBM traffic counters
+        for _ in range(3):
+            copy_dst.copy_(copy_src)
+        torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, about %.0f s)" % args.cpu_budget)
@@ -239,14 +247,15 @@ def run(args):
 
 
 def sweep(args):
-    """cfg: S in 2,3,4 x 1 or 2 producer waves on the 4096^3 fp32 GEMM."""
+    """Ring depth S in 2, 3, 4 x 1 or 2 producer waves on the 4096^3 fp32 GEMM
+    (256x128 tiles; each point takes the deepest k tile whose ring fits in LDS)."""
     import copy as _copy
     out = []
     for producers in (1, 2):
         for stages in (2, 3, 4):
             a = _copy.copy(args)
             a.stages, a.producers, a.no_copy, a.no_cpu_baseline = stages, producers, True, True
-            a.bm, a.bn, a.bk, a.consumers = a.bm or 128, a.bn or 128, a.bk or 16, a.consumers or 4
+            a.bm, a.bn, a.consumers = a.bm or 256, a.bn or 128, a.consumers or 8
             try:
                 r = run(a)
                 line = {"stages": stages, "producer_waves": producers, "tile": r["config"]["tile"],
@@ -276,9 +285,13 @@ def main():
     p.add_argument("--copy-stages", type=int, default=0)
     p.add_argument("--copy-producers", type=int, default=0)
     p.add_argument("--copy-consumers", type=int, default=0)
+    p.add_argument("--copy-cached", action="store_true",
+                   help="staged copy: ordinary (cached) loads and stores instead of streaming ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     p.add_argument("--check", action="store_true", help="also compare the copy's output on the GPU")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="after timing, run torch's plain 1 GiB device copy 3 times (for counter calibration)")
     p.add_argument("--sweep", action="store_true")
     args = p.parse_args()
     if args.gpus != 1:

@@ -49,7 +49,8 @@ extern "C" {
 #define WSG_BF16 1
 
 /* flags for wsg_config.flags */
-#define WSG_FLAG_GENERAL_PRODUCER 1 /* force the register-staged producer (any shape) over the LDS-DMA one */
+#define WSG_FLAG_GENERAL_PRODUCER 1 /* GEMM: force the register-staged producer (any shape) over the LDS-DMA one */
+#define WSG_FLAG_NONTEMPORAL 2      /* staged copy: streaming (non-temporal) loads and stores */
 
 /*
  * Launch configuration. A zero field means "choose the default". The

@@ -109,6 +109,20 @@ def _may_pass(flag: Tuple[int, int, int], parity: int) -> bool:
     return flag[0] != parity
 
 
+# A second encoding of the same barrier, for expected counts that are powers
+# of two: a plain arrival counter whose bit log2(E) is the phase bit. The
+# simulator runs either encoding through the same checks; ("counter", c)
+# flags are adapted to the (phase, pending, completed) view below.
+
+def _counter_view(count: int, expected: int) -> Tuple[int, int, int]:
+    shift = expected.bit_length() - 1
+    return ((count >> shift) & 1, expected - (count % expected), count // expected)
+
+
+def _is_pow2(x: int) -> bool:
+    return x > 0 and (x & (x - 1)) == 0
+
+
 # ---------------------------------------------------------------------------
 # Exhaustive interleavings
 # ---------------------------------------------------------------------------
@@ -117,19 +131,49 @@ def _may_pass(flag: Tuple[int, int, int], parity: int) -> bool:
 # 2 arrive on empty. Every step is one atomic scheduling point.
 
 def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
-            max_states: int = 5_000_000) -> Result:
+            max_states: int = 5_000_000, encoding: str = "phase", lookahead: int = 0) -> Result:
+    """encoding: "phase" (phase bit + pending count) or "counter" (arrival
+    counter whose bit log2(E) is the phase bit; E must be a power of two).
+
+    lookahead = 0: each producer fills a buffer and signals it in one go.
+    lookahead = D >= 1: asynchronous fills, as on the device: a producer keeps
+    up to D tiles issued but not yet signalled; before waiting for the next
+    free buffer it completes (the data lands) and signals the oldest one when
+    D are in flight, and after the last tile it drains the rest. A buffer is
+    checked for overwrite when its fill is issued; its data becomes readable
+    only when the fill completes."""
     if variant not in VARIANTS:
         raise ValueError(variant)
     one = variant == "one_barrier"
     exp_full = P + C if one else P
     exp_empty = C
+    if encoding == "counter":
+        if not (_is_pow2(exp_full) and _is_pow2(exp_empty)):
+            raise ValueError("the counter encoding needs power-of-two arrival counts")
+        # flags are stored as raw counters and viewed through _counter_view
+        def arrive(flag, expected):
+            return flag + 1
 
-    init_flag_full = (0, exp_full, 0)
-    init_flag_empty = (0, exp_empty, 0)
+        def view(flag, expected):
+            return _counter_view(flag, expected)
+        init_flag_full = 0
+        init_flag_empty = 0
+    elif encoding == "phase":
+        def arrive(flag, expected):
+            return _arrive(flag, expected)
+
+        def view(flag, expected):
+            return flag
+        init_flag_full = (0, exp_full, 0)
+        init_flag_empty = (0, exp_empty, 0)
+    else:
+        raise ValueError(encoding)
     # state: (prod pcs, cons pcs, full flags, empty flags, buffer tags)
     # pc = (tile, step); buffer tags: per buffer a tuple of P producer tags
+    if lookahead and variant == "one_barrier":
+        raise ValueError("lookahead is modelled for the two-barrier protocol only")
     init = (
-        tuple((0, 0) for _ in range(P)),
+        tuple(((0, False, 0) if lookahead else (0, 0)) for _ in range(P)),
         tuple((0, 0) for _ in range(C)),
         tuple(init_flag_full for _ in range(S)),
         tuple(init_flag_empty for _ in range(S)),
@@ -143,10 +187,71 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
     max_lead = 0
     reach = set()
 
+    def overwrite_check(i, t, s, conss):
+        for c, (tc, sc) in enumerate(conss):
+            for tt in range(tc if sc <= 1 else tc + 1, T):
+                if tt >= t:
+                    break
+                if slot_of(tt, S, variant) == s:
+                    raise ProtocolViolation(
+                        "producer %d overwrote buffer %d with tile %d while consumer %d "
+                        "had not yet read tile %d" % (i, s, t, c, tt))
+
+    def producer_moves_async(i, prod, st):
+        # prod = (next tile to issue, passed its empty wait?, tiles in flight)
+        prods, conss, fulls, empties, bufs = st
+        t, waited, inflight = prod
+        out = []
+
+        def with_prod(newp, nf=fulls, nb=bufs):
+            np_ = list(prods)
+            np_[i] = newp
+            return (tuple(np_), conss, nf, empties, nb)
+
+        if inflight == lookahead or (t >= T and inflight > 0):
+            old = t - inflight
+            so = slot_of(old, S, variant)
+            nb = list(bufs)
+            tags = list(nb[so])
+            tags[i] = old
+            nb[so] = tuple(tags)
+            nf = list(fulls)
+            nf[so] = arrive(nf[so], exp_full)
+            out.append(with_prod((t, waited, inflight - 1), tuple(nf), tuple(nb)))
+            return out
+        if t >= T:
+            return out
+        s = slot_of(t, S, variant)
+        if not 0 <= s < S:
+            raise ProtocolViolation("tile %d mapped to buffer %d outside 0..%d" % (t, s, S - 1))
+        if not waited:
+            ok = True if variant == "no_empty_wait" else _may_pass(view(empties[s], exp_empty),
+                                                                  empty_parity(t, S, variant))
+            if ok:
+                if variant != "no_empty_wait":
+                    done = view(empties[s], exp_empty)[2]
+                    if done != t // S:
+                        raise ProtocolViolation(
+                            "producer %d passed the empty wait of tile %d on completion %d, expected %d"
+                            % (i, t, done, t // S))
+                out.append(with_prod((t, True, inflight)))
+            return out
+        overwrite_check(i, t, s, conss)
+        nb = list(bufs)
+        tags = list(nb[s])
+        tags[i] = -2  # in transit: not readable until the fill completes
+        nb[s] = tuple(tags)
+        out.append(with_prod((t + 1, False, inflight + 1), fulls, tuple(nb)))
+        return out
+
     def successors(st):
         prods, conss, fulls, empties, bufs = st
         out = []
-        for i, (t, step) in enumerate(prods):
+        for i, prod in enumerate(prods):
+            if lookahead:
+                out.extend(producer_moves_async(i, prod, st))
+                continue
+            t, step = prod
             if t >= T:
                 continue
             s = slot_of(t, S, variant)
@@ -156,17 +261,18 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
                 if variant == "no_empty_wait":
                     ok = True
                 elif one:
-                    ok = _may_pass(fulls[s], empty_parity(t, S))
+                    ok = _may_pass(view(fulls[s], exp_full), empty_parity(t, S))
                 else:
-                    ok = _may_pass(empties[s], empty_parity(t, S, variant))
+                    ok = _may_pass(view(empties[s], exp_empty), empty_parity(t, S, variant))
                 if ok:
                     if not one and variant != "no_empty_wait":
                         # the release awaited is that of tile t - S
                         want = t // S
-                        if empties[s][2] != want:
+                        done = view(empties[s], exp_empty)[2]
+                        if done != want:
                             raise ProtocolViolation(
                                 "producer %d passed the empty wait of tile %d on completion %d, expected %d"
-                                % (i, t, empties[s][2], want))
+                                % (i, t, done, want))
                     np_ = list(prods)
                     np_[i] = (t, 1)
                     out.append((tuple(np_), conss, fulls, empties, bufs))
@@ -189,7 +295,7 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
                 out.append((tuple(np_), conss, fulls, empties, tuple(nb)))
             else:
                 nf = list(fulls)
-                nf[s] = _arrive(nf[s], exp_full)
+                nf[s] = arrive(nf[s], exp_full)
                 np_ = list(prods)
                 np_[i] = (t + 1, 0)
                 out.append((tuple(np_), conss, tuple(nf), empties, bufs))
@@ -200,13 +306,14 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
             if not 0 <= s < S:
                 raise ProtocolViolation("tile %d mapped to buffer %d outside 0..%d" % (t, s, S - 1))
             if step == 0:
-                if _may_pass(fulls[s], full_parity(t, S, variant)):
+                if _may_pass(view(fulls[s], exp_full), full_parity(t, S, variant)):
                     if not one:
                         want = t // S + 1
-                        if fulls[s][2] != want:
+                        done = view(fulls[s], exp_full)[2]
+                        if done != want:
                             raise ProtocolViolation(
                                 "consumer %d passed the full wait of tile %d on completion %d, expected %d"
-                                % (j, t, fulls[s][2], want))
+                                % (j, t, done, want))
                     nc = list(conss)
                     nc[j] = (t, 1)
                     out.append((prods, tuple(nc), fulls, empties, bufs))
@@ -225,11 +332,11 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
                     out.append((prods, tuple(nc), fulls, empties, bufs))
                 elif one:
                     nf = list(fulls)
-                    nf[s] = _arrive(nf[s], exp_full)
+                    nf[s] = arrive(nf[s], exp_full)
                     out.append((prods, tuple(nc), tuple(nf), empties, bufs))
                 else:
                     ne = list(empties)
-                    ne[s] = _arrive(ne[s], exp_empty)
+                    ne[s] = arrive(ne[s], exp_empty)
                     out.append((prods, tuple(nc), fulls, tuple(ne), bufs))
         return out
 
@@ -242,8 +349,12 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
             if len(seen) > max_states:
                 raise RuntimeError("state space above %d states" % max_states)
             prods, conss = st[0], st[1]
-            filled = min(t if step < 2 else t + 1 for t, step in prods) if prods else 0
-            begun = max(t if step >= 1 else t - 1 for t, step in prods)
+            if lookahead:
+                filled = min(p[0] - p[2] for p in prods)
+                begun = max(p[0] - 1 for p in prods)
+            else:
+                filled = min(t if step < 2 else t + 1 for t, step in prods) if prods else 0
+                begun = max(t if step >= 1 else t - 1 for t, step in prods)
             released = min(t for t, step in conss)
             max_lead = max(max_lead, filled - released)
             for t, step in conss:
@@ -251,7 +362,8 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
                     reach.add((t, begun))
             succ = successors(st)
             if not succ:
-                if not all(t >= T for t, _ in prods) or not all(t >= T for t, _ in conss):
+                prods_done = all((p[0] >= T and p[2] == 0) if lookahead else p[0] >= T for p in prods)
+                if not prods_done or not all(t >= T for t, _ in conss):
                     deadlock = True
                 continue
             stack.extend(succ)

@@ -66,7 +66,7 @@ WORKLOADS = {
             tile_bytes=64 * 1024, stages=2,
             name="LDS-staged copy of 1 GiB fp32, 64 KiB tiles, 2-stage ring"),
     3: dict(kind="gemm", dtype="fp32", M=4096, N=4096, K=4096, dist="uniform",
-            stages=4,
+            stages=2, stage_sweep=(2, 3, 4),
             name="fp32 gemm+bias+relu 4096x4096x4096"),
     4: dict(kind="gemm", dtype="fp32", M=3000, N=5000, K=4100, dist="uniform",
             stages=4,

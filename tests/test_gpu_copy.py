@@ -50,6 +50,10 @@ def test_copy_sizes(gpu, n, stages):
     (dict(copy_tile_bytes=16384, producer_waves=2, consumer_waves=2), 8),
     (dict(copy_tile_bytes=16384, producer_waves=1, consumer_waves=1), 5),
     (dict(copy_tile_bytes=4096, producer_waves=1, consumer_waves=1), 16),
+    (dict(copy_tile_bytes=16384, producer_waves=1, consumer_waves=1, flags=2), 8),
+    (dict(copy_tile_bytes=8192, producer_waves=1, consumer_waves=1, flags=2), 16),
+    (dict(copy_tile_bytes=65536, producer_waves=4, consumer_waves=4, flags=2), 2),
+    (dict(copy_tile_bytes=32768, producer_waves=2, consumer_waves=2, flags=2), 4),
 ])
 def test_copy_configs_multi_lap(gpu, config, stages):
     # enough tiles that every workgroup laps its ring several times, plus a ragged tail
@@ -82,8 +86,11 @@ def test_copy_argument_errors(gpu):
     import torch
     x = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
     assert gpu.lib.staged_copy(x.data_ptr(), x.data_ptr() + 4096, 8192, 2) == gpu.WSG_EINVAL  # overlap
-    with pytest.raises(gpu.WsgError) as e:
-        gpu.staged_copy(x[:65536], x[65536:131072], stages=3)  # 3 x 64 KiB exceeds LDS
+    with pytest.raises(gpu.WsgError) as e:  # 3 x 64 KiB exceeds LDS
+        gpu.staged_copy_ex(x[:65536], x[65536:131072], stages=3, config=dict(copy_tile_bytes=65536))
+    assert e.value.code == gpu.WSG_EUNSUPPORTED
+    with pytest.raises(gpu.WsgError) as e:  # 20 x 8 KiB exceeds LDS even at the smallest default slot
+        gpu.staged_copy(x[:65536], x[65536:131072], stages=20)
     assert e.value.code == gpu.WSG_EUNSUPPORTED
     with pytest.raises(gpu.WsgError) as e:
         gpu.staged_copy_ex(x[:1024], x[2048:3072], stages=2, config=dict(copy_tile_bytes=12345))

@@ -122,3 +122,55 @@ def test_jitter_keeps_order_and_bounds():
     assert all(tl.start[i] >= tl.land[i] for i in range(300))
     assert all(tl.start[i] >= tl.end[i - 1] for i in range(1, 300))
     assert all(tl.issue[i] >= tl.release[i - 3] for i in range(3, 300))
+
+
+POW2_CASES = [(S, T, P, C) for S in (1, 2, 3, 4) for T in (3, 6) for P in (1, 2) for C in (1, 2, 4)
+              if not (S >= 3 and T == 6 and P * C >= 8)]
+
+
+@pytest.mark.parametrize("S,T,P,C", POW2_CASES)
+def test_counter_encoding_matches_phase_encoding(S, T, P, C):
+    """The device's flag word (an arrival counter whose bit log2(E) is the
+    phase bit) behaves exactly like the phase-bit + pending-count barrier."""
+    a = rs.explore(S, T, P, C)
+    b = rs.explore(S, T, P, C, encoding="counter")
+    assert b.violation is None and not b.deadlock
+    assert (a.states, a.max_lead, a.reach_pairs) == (b.states, b.max_lead, b.reach_pairs)
+
+
+@pytest.mark.parametrize("variant", ["empty_same_parity", "drop_release", "slot_div2", "no_empty_wait",
+                                     "full_parity_flipped"])
+def test_counter_encoding_negative_controls(variant):
+    r = rs.explore(2, 6, 1, 2, variant=variant, encoding="counter")
+    assert r.deadlock or r.violation is not None
+
+
+def test_counter_encoding_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        rs.explore(2, 4, 3, 1, encoding="counter")
+
+
+LOOKAHEAD_CASES = [(S, T, P, C, D) for S in (1, 2, 3, 4) for T in (4, 7) for P in (1, 2) for C in (1, 2)
+                   for D in range(1, S + 1) if not (S >= 3 and T == 7 and P == 2)]
+
+
+@pytest.mark.parametrize("S,T,P,C,D", LOOKAHEAD_CASES)
+def test_async_fill_lookahead_up_to_S_is_safe_and_live(S, T, P, C, D):
+    """The device producer keeps up to D fills in flight and publishes the
+    oldest before waiting for the next free buffer; any D <= S is correct."""
+    r = rs.explore(S, T, P, C, lookahead=D, encoding="counter")
+    assert r.violation is None and not r.deadlock
+    assert r.max_lead <= S
+
+
+@pytest.mark.parametrize("S", [1, 2, 3])
+def test_async_fill_lookahead_beyond_S_deadlocks(S):
+    r = rs.explore(S, 2 * S + 3, 1, 1, lookahead=S + 1)
+    assert r.deadlock
+
+
+@pytest.mark.parametrize("variant", ["empty_same_parity", "drop_release", "slot_div2", "no_empty_wait",
+                                     "full_parity_flipped"])
+def test_async_fill_negative_controls(variant):
+    r = rs.explore(2, 6, 1, 2, variant=variant, lookahead=1)
+    assert r.deadlock or r.violation is not None

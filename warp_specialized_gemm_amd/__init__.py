@@ -20,7 +20,7 @@ __all__ = [
     "WsgError", "Config", "lib", "library_path", "EXPORTS",
     "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "resolve_config",
     "staged_copy", "staged_copy_ex", "check_device_status", "set_stream", "get_stream",
-    "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER",
+    "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +34,7 @@ WSG_ETIMEOUT = -4
 WSG_FP32 = 0
 WSG_BF16 = 1
 WSG_FLAG_GENERAL_PRODUCER = 1
+WSG_FLAG_NONTEMPORAL = 2
 
 # every function include/wsg.h declares
 EXPORTS = (

@@ -59,11 +59,13 @@ struct GemmArgs {
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Give each XCD a contiguous run of logical tiles, then walk those in
-// groups of kGroupRows tile rows so the tiles resident on one XCD share rows
-// of A and columns of B.
+// groups of a few tile rows so the tiles resident on one XCD at a time share
+// rows of A and columns of B.
 constexpr int kXcds = 8;
-constexpr int kGroupRows = 8;
 
+// kGroupRows tile rows per group: 8 for square tiles; for tall tiles fewer
+// rows (and so more columns) keep the A and B bytes a group touches balanced.
+template <int kGroupRows>
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int G = tiles_m * tiles_n;
     const int x = bid % kXcds, i = bid / kXcds;
@@ -275,6 +277,63 @@ struct BTransBf16 {
 };
 
 // ----------------------------------------------------------------------------
+// Consumer walk over the ring, shared by both kernels. The K loop is cut into
+// U = T * KG groups of 16 k; the fragments of group u + 1 are read while the
+// MFMAs of group u run. A slot is released (one arrival on its empty flag)
+// once the reads of its last group have completed. The full flag of the next
+// tile is read early, together with the last group's fragments, and only if
+// that early value shows the tile unpublished does the wave spin on it.
+// Returns false if a wait gave up.
+// ----------------------------------------------------------------------------
+template <int KG, int P, typename Frag, typename Read, typename Mma>
+__device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, int slot_bytes, uint32_t fb,
+                                             unsigned *status, Read read, Mma mma) {
+    const uint32_t *flagp = reinterpret_cast<const uint32_t *>(ring - kFlagBytes);
+    const int U = T * KG;
+    if (U == 0) return true;
+    Frag f0, f1;
+    int rs = 0, rg = 0;  // slot and group of the latest read
+    uint32_t rlap = 0;
+    int cs = 0;          // slot being consumed
+    uint32_t peek = 0;   // early value of the next tile's full flag
+    if (!flag_wait<P>(full_flag(fb, 0), 0u, status, kStatusGemm)) return false;
+    read(f0, ring, 0);
+    if (KG == 1 && U > 1) peek = flag_peek(flagp + (S > 1 ? 1 : 0));
+    bool alive = true;
+    auto step = [&](int u, Frag &cur, Frag &nxt) {
+        wait_lgkm0();  // the reads of group u (and the early flag value) have landed
+        if (u % KG == KG - 1) {
+            flag_arrive(empty_flag(fb, cs));
+            if (++cs == S) cs = 0;
+        }
+        if (u + 1 < U) {
+            if (++rg == KG) {
+                rg = 0;
+                if (++rs == S) {
+                    rs = 0;
+                    ++rlap;
+                }
+                if (phase_of<P>(__builtin_amdgcn_readfirstlane(peek)) == (rlap & 1u)) {
+                    if (!flag_wait<P>(full_flag(fb, rs), rlap & 1u, status, kStatusGemm)) {
+                        alive = false;
+                        return;
+                    }
+                }
+                asm volatile("" ::: "memory");
+            }
+            read(nxt, ring + (size_t)rs * slot_bytes, rg);
+            if (rg == KG - 1 && u + 1 + KG < U) peek = flag_peek(flagp + (rs + 1 == S ? 0 : rs + 1));
+        }
+        mma(cur);
+    };
+    for (int u = 0; alive && u < U; u += 2) {
+        step(u, f0, f1);
+        if (alive && u + 1 < U) step(u + 1, f1, f0);
+    }
+    return alive;
+}
+
+// ----------------------------------------------------------------------------
 // fp32 kernel
 // ----------------------------------------------------------------------------
 template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA>
@@ -301,7 +360,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     __syncthreads();  // the only workgroup barrier
 
     int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    tile_coords<(8 * BN / BM > 0 ? 8 * BN / BM : 1)>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int T = (int)((K + BK - 1) / BK);
@@ -318,36 +377,46 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
             BD bd;
             ad.init(wave, lane, K, rows_valid);
             bd.init(wave, lane, N, n0);
-            const int D = min(S - 1, 63 / NL);
+            // Up to D tiles in flight. The oldest is completed and published
+            // before the wait for the next free slot, so a full signal never
+            // waits on an empty one (the producer spends the steady state of a
+            // compute-bound kernel blocked on empty slots).
+            const int D = max(1, min(S - 1, 63 / NL));
+            int inflight = 0, ps = 0;  // tiles issued but not published; slot of the oldest
             for (int t = 0; t < T; ++t) {
-                if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
+                if (inflight == D) {
+                    wait_vmcnt_dyn((D - 1) * NL);
+                    flag_arrive(full_flag(fb, ps));
+                    if (++ps == S) ps = 0;
+                    --inflight;
+                }
+                if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
                 const int64_t k0 = (int64_t)t * BK;
                 unsigned char *slot = ring + (size_t)s * SLOT;
                 ad.issue(slot, wave, A_rows, rows_valid, K, k0);
                 bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
-                if (t >= D) {
-                    wait_vmcnt_dyn(D * NL);
-                    flag_arrive(full_flag(fb, (t - D) % S), P);
-                }
+                ++inflight;
                 if (++s == S) {
                     s = 0;
                     ++lap;
                 }
             }
-            for (int t = max(0, T - D); t < T; ++t) {
-                wait_vmcnt_dyn((T - 1 - t) * NL);
-                flag_arrive(full_flag(fb, t % S), P);
+            while (inflight > 0) {
+                wait_vmcnt_dyn((inflight - 1) * NL);
+                flag_arrive(full_flag(fb, ps));
+                if (++ps == S) ps = 0;
+                --inflight;
             }
         } else {
             for (int t = 0; t < T; ++t) {
-                if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
+                if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
                 const int64_t k0 = (int64_t)t * BK;
                 unsigned char *slot = ring + (size_t)s * SLOT;
                 a_general<BM, BK, 4, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
                 b_general_f32<BN, BK, P>(slot + A_BYTES, wave, lane, reinterpret_cast<const float *>(a.B), N, K, n0,
                                          k0);
                 wait_lgkm0();
-                flag_arrive(full_flag(fb, s), P);
+                flag_arrive(full_flag(fb, s));
                 if (++s == S) {
                     s = 0;
                     ++lap;
@@ -407,45 +476,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[i][jj], f.b[j][jj], acc[i][j], 0, 0, 0);
     };
 
-    // Reads run one k group ahead of the MFMAs.
-    const int U = T * KG;
-    Frag f0, f1;
-    int rs = 0, rg = 0;       // slot and group of the next read
-    uint32_t rlap = 0;
-    int cs = 0;               // slot being consumed
-    bool alive = true;
-    if (U > 0) {
-        alive = flag_wait(full_flag(fb, 0), 0u, a.status, kStatusGemm);
-        if (alive) read(f0, ring, 0);
-    }
-    auto step = [&](int u, Frag &cur, Frag &nxt) {
-        wait_lgkm0();  // the reads of group u are in registers
-        const int g = u % KG;
-        if (g == KG - 1) {
-            flag_arrive(empty_flag(fb, cs), NCW);
-            if (++cs == S) cs = 0;
-        }
-        if (u + 1 < U) {
-            if (++rg == KG) {
-                rg = 0;
-                if (++rs == S) {
-                    rs = 0;
-                    ++rlap;
-                }
-                if (!flag_wait(full_flag(fb, rs), rlap & 1u, a.status, kStatusGemm)) {
-                    alive = false;
-                    return;
-                }
-            }
-            read(nxt, ring + (size_t)rs * SLOT, rg);
-        }
-        mma(cur);
-    };
-    for (int u = 0; alive && u < U; u += 2) {
-        step(u, f0, f1);
-        if (alive && u + 1 < U) step(u + 1, f1, f0);
-    }
-    if (!alive) return;
+    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, read, mma)) return;
 
     // epilogue: C = relu(acc + bias[n]); lane (li, q) holds column li and rows
     // 4q + r of each 16x16 block
@@ -506,7 +537,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
     __syncthreads();  // the only workgroup barrier
 
     int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    tile_coords<(8 * BN / BM > 0 ? 8 * BN / BM : 1)>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int T = (int)((K + BK - 1) / BK);
@@ -514,11 +545,10 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
 
     if (wave < P) {
         // ================= producer =================
-        // Tile t's loads are issued right after tile t - 1 is transposed and
-        // published; they land while the producer waits for the next free
-        // slot, so with S > 1 one tile of global latency hides behind that
-        // wait. (With S = 1 the next fill needs this tile consumed first, so
-        // each tile is published before the loop moves on.)
+        // Tile t - 1 is transposed and published before the wait for tile t's
+        // slot, then tile t's loads are issued: they land while the producer
+        // waits for the next free slot, and no full signal waits on an empty
+        // one.
         const int rows_valid = (int)min((int64_t)BM, M - m0);
         const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * 2u;
         const uint16_t *B = reinterpret_cast<const uint16_t *>(a.B);
@@ -540,24 +570,22 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
             wait_vmcnt<0>();  // only this tile's loads are outstanding
             bt.store(ring + (size_t)s * SLOT + A_BYTES, wave, lane);
             wait_lgkm0();
-            flag_arrive(full_flag(fb, s), P);
+            flag_arrive(full_flag(fb, s));
         };
-        const bool ahead = S > 1;
         int s = 0;
         uint32_t lap = 0;
         int ps = 0;  // slot of the tile awaiting publication
         for (int t = 0; t < T; ++t) {
-            if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
-            if (ahead && t > 0) publish(ps);
+            if (t > 0) publish(ps);
+            if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
             issue(t, s);
-            if (!ahead) publish(s);
             ps = s;
             if (++s == S) {
                 s = 0;
                 ++lap;
             }
         }
-        if (ahead && T > 0) publish(ps);
+        if (T > 0) publish(ps);
         return;
     }
 
@@ -605,44 +633,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
 
-    const int U = T * KG;
-    Frag f0, f1;
-    int rs = 0, rg = 0;
-    uint32_t rlap = 0;
-    int cs = 0;
-    bool alive = true;
-    if (U > 0) {
-        alive = flag_wait(full_flag(fb, 0), 0u, a.status, kStatusGemm);
-        if (alive) read(f0, ring, 0);
-    }
-    auto step = [&](int u, Frag &cur, Frag &nxt) {
-        wait_lgkm0();
-        const int g = u % KG;
-        if (g == KG - 1) {
-            flag_arrive(empty_flag(fb, cs), NCW);
-            if (++cs == S) cs = 0;
-        }
-        if (u + 1 < U) {
-            if (++rg == KG) {
-                rg = 0;
-                if (++rs == S) {
-                    rs = 0;
-                    ++rlap;
-                }
-                if (!flag_wait(full_flag(fb, rs), rlap & 1u, a.status, kStatusGemm)) {
-                    alive = false;
-                    return;
-                }
-            }
-            read(nxt, ring + (size_t)rs * SLOT, rg);
-        }
-        mma(cur);
-    };
-    for (int u = 0; alive && u < U; u += 2) {
-        step(u, f0, f1);
-        if (alive && u + 1 < U) step(u + 1, f1, f0);
-    }
-    if (!alive) return;
+    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, read, mma)) return;
 
     // epilogue: lane (li, h) holds column li of each 32x32 block and rows
     // 8*(r/4) + 4*h + (r%4) of its 16 registers
@@ -688,16 +679,17 @@ namespace {
     {WSG_BF16, BM, BN, BK, P, CWM, CWN, DMA,                                                               \
      reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA>)}
 
-// First match wins when the caller leaves fields at 0, so each group starts
-// with its default.
+// When the caller leaves fields at 0, the first variant (in this order) whose
+// tile matches the size class and whose ring fits in LDS wins.
 const GemmVariant kGemmVariants[] = {
-    WSG_F32(256, 128, 16, 2, 4, 2, true),  WSG_F32(128, 128, 16, 1, 2, 2, true),
+    WSG_F32(256, 128, 32, 2, 4, 2, true),  WSG_F32(256, 128, 16, 2, 4, 2, true),
+    WSG_F32(128, 128, 32, 2, 2, 2, true),  WSG_F32(128, 128, 16, 1, 2, 2, true),
     WSG_F32(128, 128, 16, 2, 2, 2, true),  WSG_F32(128, 256, 16, 2, 2, 4, true),
-    WSG_F32(128, 128, 32, 2, 2, 2, true),  WSG_F32(256, 128, 32, 2, 4, 2, true),
-    WSG_F32(64, 64, 16, 1, 2, 2, true),    WSG_F32(256, 128, 16, 2, 4, 2, false),
+    WSG_F32(64, 64, 16, 1, 2, 2, true),    WSG_F32(256, 128, 32, 1, 4, 2, true),
+    WSG_F32(256, 128, 16, 1, 4, 2, true),  WSG_F32(256, 128, 16, 2, 4, 2, false),
     WSG_F32(128, 128, 16, 1, 2, 2, false), WSG_F32(64, 64, 16, 1, 2, 2, false),
-    WSG_BF(256, 128, 32, 1, 2, 2, true),   WSG_BF(128, 128, 32, 1, 2, 2, true),
-    WSG_BF(256, 128, 64, 2, 2, 2, true),   WSG_BF(64, 64, 32, 1, 2, 2, true),
+    WSG_BF(256, 128, 64, 2, 2, 2, true),   WSG_BF(256, 128, 32, 1, 2, 2, true),
+    WSG_BF(128, 128, 32, 1, 2, 2, true),   WSG_BF(64, 64, 32, 1, 2, 2, true),
     WSG_BF(256, 128, 32, 1, 2, 2, false),  WSG_BF(128, 128, 32, 1, 2, 2, false),
     WSG_BF(64, 64, 32, 1, 2, 2, false),
 };
@@ -739,6 +731,7 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     const bool aligned = K % align_elems == 0 && N % align_elems == 0 && ((uintptr_t)A % 16) == 0 &&
                          ((uintptr_t)B % 16) == 0;
     const GemmVariant *pick = nullptr;
+    bool lds_short = false;
     for (int pass = 0; pass < 2 && !pick; ++pass) {
         const bool want_dma = pass == 0;
         if (want_dma && (force_general || !aligned)) continue;
@@ -748,9 +741,19 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
             if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW)) continue;
             if (want_dma && ((int64_t)v.BM * K * esz >= 0x7FFFFFFF || (int64_t)v.BK * N * esz >= 0x7FFFFFFF))
                 continue;
+            const size_t need = (size_t)kFlagBytes + (size_t)stages * (size_t)(v.BM * v.BK + v.BK * v.BN) * esz;
+            if (need > dev.max_lds) {
+                lds_short = true;  // a smaller BK of the same tile may still fit
+                continue;
+            }
             pick = &v;
             break;
         }
+    }
+    if (!pick && lds_short) {
+        *err = "no built " + std::to_string(BM) + "x" + std::to_string(BN) + " tile fits a " + std::to_string(stages) +
+               "-stage ring in the " + std::to_string(dev.max_lds) + " bytes of LDS a workgroup may use";
+        return WSG_EUNSUPPORTED;
     }
     if (!pick) {
         *err = "no GEMM kernel built for tile " + std::to_string(BM) + "x" + std::to_string(BN) + "x" +

@@ -16,18 +16,20 @@
 //   * producers wait "empty" for the release of tile t - S, i.e. with parity
 //     ((t / S) & 1) ^ 1, which passes at once on the first lap.
 //
-// gfx950 has neither TMA nor mbarrier: a flag is one 32-bit LDS word.
-//   bits [15:0]  arrivals in the current phase
-//   bits [31:16] completed phases (mod 2^16); bit 16 is the phase bit.
-// The last arrival adds (1 << 16) - expected, which clears the count and
-// flips the phase bit in one add. Waves of one workgroup are co-resident, so
-// spinning on an LDS word is safe; every wait is bounded and records a
-// timeout in a device status word instead of hanging.
+// gfx950 has neither TMA nor mbarrier: a flag is one 32-bit LDS word that
+// counts arrivals. Expected arrival counts are powers of two (E = 1, 2, 4, 8
+// waves), so E arrivals complete a phase exactly when bit log2(E) of the
+// counter flips: that bit is the phase bit. An arrival is then a single
+// LDS add with no return value and nothing to wait for. Waves of one
+// workgroup are co-resident, so spinning on an LDS word is safe; every wait
+// is bounded and records a timeout in a device status word instead of
+// hanging.
 //
-// Flag accesses are inline assembly with their own lgkmcnt wait. The
-// compiler treats any LDS access that follows an LDS-DMA load as possibly
-// aliasing it and puts a vmcnt(0) in front, which would drain the producer's
-// loads in flight; the assembly keeps those loads outstanding.
+// Producer-side flag accesses are inline assembly with their own lgkmcnt
+// wait: the compiler treats any LDS access that follows an LDS-DMA load as
+// possibly aliasing it and puts a vmcnt(0) in front, which would drain the
+// loads in flight. Consumers, which issue no LDS-DMA, may also read a flag
+// ahead of time with an ordinary atomic load and test it later.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,8 +37,6 @@
 
 namespace wsg {
 
-constexpr uint32_t kFlagCountMask = 0xFFFFu;
-constexpr uint32_t kPhaseOne = 1u << 16;
 constexpr uint32_t kSpinLimit = 1u << 25;  // about a second of polling
 constexpr int kFlagBytes = 256;            // LDS bytes reserved for flags at offset 0
 constexpr int kMaxStages = 32;             // full[32] + empty[32] words fit in kFlagBytes
@@ -62,13 +62,27 @@ __device__ __forceinline__ uint32_t flag_load(uint32_t addr) {
 __device__ __forceinline__ uint32_t full_flag(uint32_t base, int s) { return base + 4u * (uint32_t)s; }
 __device__ __forceinline__ uint32_t empty_flag(uint32_t base, int s) { return base + 128u + 4u * (uint32_t)s; }
 
-// Proceed once the phase bit of the flag differs from `parity`. Returns false
-// (after recording the timeout) when the wait gives up.
+template <int E>
+constexpr int log2_arrivals() {
+    static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16, "expected arrivals must be a power of two");
+    return E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : E == 8 ? 3 : 4;
+}
+
+// Phase bit of a flag word whose phases complete every E arrivals.
+template <int E>
+__device__ __forceinline__ uint32_t phase_of(uint32_t word) {
+    return (word >> log2_arrivals<E>()) & 1u;
+}
+
+// Proceed once the phase bit differs from `parity`, i.e. once the phase of
+// that parity has completed. Returns false (after recording the timeout)
+// when the wait gives up.
+template <int E>
 __device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsigned *status, unsigned who) {
     uint32_t spins = 0;
     while (true) {
-        uint32_t v = __builtin_amdgcn_readfirstlane(flag_load(addr));
-        if (((v >> 16) & 1u) != parity) return true;
+        const uint32_t v = __builtin_amdgcn_readfirstlane(flag_load(addr));
+        if (phase_of<E>(v) != parity) return true;
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
             if ((threadIdx.x & 63) == 0) atomicOr(status, kStatusTimeout | who);
@@ -77,23 +91,18 @@ __device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsign
     }
 }
 
-// One arrival of the calling wave (lane 0 does the atomic). The caller has
-// already waited for the wave's own LDS writes or reads of the slot.
-__device__ __forceinline__ void flag_arrive(uint32_t addr, uint32_t expected) {
+// One arrival of the calling wave (lane 0 adds 1). The caller has already
+// waited for the wave's own LDS writes or reads of the slot; LDS operations
+// of one wave execute in order, so nothing here needs waiting for.
+__device__ __forceinline__ void flag_arrive(uint32_t addr) {
     if ((threadIdx.x & 63) != 0) return;
-    if (expected == 1) {
-        asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(kPhaseOne) : "memory");
-        return;
-    }
-    uint32_t old;
-    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(old)
-                 : "v"(addr), "v"(1u)
-                 : "memory");
-    if ((old & kFlagCountMask) == expected - 1) {
-        asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(kPhaseOne - expected)
-                     : "memory");
-    }
+    asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
+}
+
+// Consumer-side early read of a flag word (no LDS-DMA in flight in the
+// calling wave); the compiler waits for it where the value is used.
+__device__ __forceinline__ uint32_t flag_peek(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // All of this wave's LDS operations done. The builtin (not inline assembly)
@@ -134,10 +143,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 constexpr uint32_t kOobOffset = 0x80000000u;  // above any num_records the library builds
 
+constexpr int kAuxNontemporal = 2;  // cache-policy bits of a buffer load: nt (streaming)
+
 // 16 bytes per lane, global -> LDS without passing through VGPRs. Lane l's
 // data lands at lds_wave_base + 16 * l (lds_wave_base is wave-uniform).
+template <int AUX = 0>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, void *lds_wave_base, uint32_t voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_wave_base, 16, voffset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_wave_base, 16, voffset, 0, 0, AUX);
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }

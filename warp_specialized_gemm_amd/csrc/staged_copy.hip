@@ -18,7 +18,11 @@
 
 namespace wsg {
 
-template <int P, int C, int TILE>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// NT: stream both directions past the caches (non-temporal loads into LDS
+// and non-temporal stores), since each byte is touched exactly once.
+template <int P, int C, int TILE, bool NT>
 __global__ void __launch_bounds__((P + C) * 64)
     staged_copy_kernel(const unsigned char *__restrict__ src, unsigned char *__restrict__ dst, uint64_t bytes,
                        uint64_t ntiles, int S, unsigned *status) {
@@ -43,7 +47,10 @@ __global__ void __launch_bounds__((P + C) * 64)
 
     if (wave < P) {
         // ---------------- producer ----------------
-        const int D = min(S - 1, 63 / NL);  // tiles kept in flight beyond the one being completed
+        // Up to D tiles in flight; the oldest is completed and published
+        // before the wait for the next free slot, so a full signal never
+        // waits on an empty one.
+        const int D = max(1, min(S - 1, 63 / NL));
         auto finish = [&](int64_t j) {
             const int s = (int)(j % S);
             const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
@@ -58,12 +65,18 @@ __global__ void __launch_bounds__((P + C) * 64)
                 wait_vmcnt<0>();
                 wait_lgkm0();
             }
-            flag_arrive(full_flag(fb, s), P);
+            flag_arrive(full_flag(fb, s));
         };
         int s = 0;
         uint32_t lap = 0;
+        int inflight = 0;
         for (int64_t j = 0; j < nloc; ++j) {
-            if (!flag_wait(empty_flag(fb, s), (lap & 1u) ^ 1u, status, kStatusCopy)) return;
+            if (inflight == D) {
+                wait_vmcnt_dyn((D - 1) * NL);
+                finish(j - D);
+                --inflight;
+            }
+            if (!flag_wait<C>(empty_flag(fb, s), (lap & 1u) ^ 1u, status, kStatusCopy)) return;
             const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
             const uint64_t valid = min((uint64_t)TILE, bytes - base);
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + base, (uint32_t)(valid & ~(uint64_t)15));
@@ -71,18 +84,15 @@ __global__ void __launch_bounds__((P + C) * 64)
 #pragma unroll
             for (int r = 0; r < NL; ++r) {
                 const uint32_t off = (uint32_t)(r * P + wave) * 1024u;
-                lds_dma16(rs, slot + off, off + 16u * lane);
+                lds_dma16<NT ? kAuxNontemporal : 0>(rs, slot + off, off + 16u * lane);
             }
-            if (j >= D) {
-                wait_vmcnt_dyn(D * NL);
-                finish(j - D);
-            }
+            ++inflight;
             if (++s == S) {
                 s = 0;
                 ++lap;
             }
         }
-        for (int64_t j = max((int64_t)0, nloc - D); j < nloc; ++j) {
+        for (int64_t j = nloc - inflight; j < nloc; ++j) {
             wait_vmcnt_dyn((int)(nloc - 1 - j) * NL);
             finish(j);
         }
@@ -92,21 +102,26 @@ __global__ void __launch_bounds__((P + C) * 64)
         int s = 0;
         uint32_t lap = 0;
         for (int64_t j = 0; j < nloc; ++j) {
-            if (!flag_wait(full_flag(fb, s), lap & 1u, status, kStatusCopy)) return;
+            if (!flag_wait<P>(full_flag(fb, s), lap & 1u, status, kStatusCopy)) return;
             const unsigned char *slot = ring + (size_t)s * TILE;
             uint4 v[NC];
 #pragma unroll
             for (int r = 0; r < NC; ++r)
                 v[r] = *reinterpret_cast<const uint4 *>(slot + (size_t)(r * C + cw) * 1024u + 16u * lane);
             wait_lgkm0();
-            flag_arrive(empty_flag(fb, s), C);
+            flag_arrive(empty_flag(fb, s));
             const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
             const uint64_t valid = min((uint64_t)TILE, bytes - base);
             unsigned char *out = dst + base;
             if (valid == (uint64_t)TILE) {
 #pragma unroll
-                for (int r = 0; r < NC; ++r)
-                    *reinterpret_cast<uint4 *>(out + (size_t)(r * C + cw) * 1024u + 16u * lane) = v[r];
+                for (int r = 0; r < NC; ++r) {
+                    unsigned char *o = out + (size_t)(r * C + cw) * 1024u + 16u * lane;
+                    if constexpr (NT)
+                        __builtin_nontemporal_store(u32x4{v[r].x, v[r].y, v[r].z, v[r].w}, reinterpret_cast<u32x4 *>(o));
+                    else
+                        *reinterpret_cast<uint4 *>(o) = v[r];
+                }
             } else {
 #pragma unroll
                 for (int r = 0; r < NC; ++r) {
@@ -134,15 +149,20 @@ namespace {
 
 struct CopyVariant {
     int P, C, tile;
+    bool nt;
     const void *kernel;
 };
 
-#define WSG_COPY_VARIANT(P, C, T) {P, C, T, reinterpret_cast<const void *>(&staged_copy_kernel<P, C, T>)}
+#define WSG_COPY_VARIANT(P, C, T, NT) {P, C, T, NT, reinterpret_cast<const void *>(&staged_copy_kernel<P, C, T, NT>)}
 
+// First match per (tile, nt) is the default wave split for that tile.
 const CopyVariant kCopyVariants[] = {
-    WSG_COPY_VARIANT(4, 4, 65536), WSG_COPY_VARIANT(2, 2, 65536), WSG_COPY_VARIANT(8, 8, 65536),
-    WSG_COPY_VARIANT(4, 8, 65536), WSG_COPY_VARIANT(4, 4, 32768), WSG_COPY_VARIANT(2, 2, 32768),
-    WSG_COPY_VARIANT(2, 2, 16384), WSG_COPY_VARIANT(1, 1, 16384), WSG_COPY_VARIANT(1, 1, 4096),
+    WSG_COPY_VARIANT(8, 8, 65536, true),   WSG_COPY_VARIANT(4, 4, 65536, true),  WSG_COPY_VARIANT(2, 2, 32768, true),
+    WSG_COPY_VARIANT(2, 2, 16384, true),   WSG_COPY_VARIANT(1, 1, 16384, true),  WSG_COPY_VARIANT(1, 1, 8192, true),
+    WSG_COPY_VARIANT(4, 4, 65536, false),  WSG_COPY_VARIANT(2, 2, 65536, false), WSG_COPY_VARIANT(8, 8, 65536, false),
+    WSG_COPY_VARIANT(4, 8, 65536, false),  WSG_COPY_VARIANT(4, 4, 32768, false), WSG_COPY_VARIANT(2, 2, 32768, false),
+    WSG_COPY_VARIANT(2, 2, 16384, false),  WSG_COPY_VARIANT(1, 1, 16384, false), WSG_COPY_VARIANT(1, 1, 8192, false),
+    WSG_COPY_VARIANT(1, 1, 4096, false),   WSG_COPY_VARIANT(1, 1, 4096, true),
 };
 
 }  // namespace
@@ -150,9 +170,19 @@ const CopyVariant kCopyVariants[] = {
 int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo &dev, CopyPlan *plan,
               std::string *err) {
     (void)bytes;
-    int tile = (cfg && cfg->copy_tile_bytes) ? cfg->copy_tile_bytes : 65536;
+    int tile = (cfg && cfg->copy_tile_bytes) ? cfg->copy_tile_bytes : 0;
     int P = (cfg && cfg->producer_waves) ? cfg->producer_waves : 0;
     int C = (cfg && cfg->consumer_waves) ? cfg->consumer_waves : 0;
+    bool nt = cfg && (cfg->flags & WSG_FLAG_NONTEMPORAL);
+    if (!cfg) {
+        // defaults: the largest slot that lets `stages` slots share 128 KiB of
+        // LDS, streamed past the caches (the fastest measured settings)
+        nt = true;
+        tile = 65536;
+        while (tile > 8192 && (size_t)stages * (size_t)tile > 131072) tile /= 2;
+    } else if (!tile) {
+        tile = 65536;
+    }
     if (stages < 1) {
         *err = "stages must be >= 1";
         return WSG_EINVAL;
@@ -163,7 +193,7 @@ int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo 
     }
     const CopyVariant *pick = nullptr;
     for (const CopyVariant &v : kCopyVariants) {
-        if (v.tile != tile) continue;
+        if (v.tile != tile || v.nt != nt) continue;
         if (P && v.P != P) continue;
         if (C && v.C != C) continue;
         pick = &v;
