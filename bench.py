@@ -139,9 +139,10 @@ def run(args):
     dtype = w["dtype"]
     stages = args.stages or w["stages"]
     config = None
-    if any(v for v in (args.bm, args.bn, args.bk, args.producers, args.consumers)):
+    if any(v for v in (args.bm, args.bn, args.bk, args.producers, args.consumers, args.group_k)):
         config = dict(BM=args.bm or 0, BN=args.bn or 0, BK=args.bk or 0,
-                      producer_waves=args.producers or 0, consumer_waves=args.consumers or 0)
+                      producer_waves=args.producers or 0, consumer_waves=args.consumers or 0,
+                      group_k=args.group_k or 0)
     resolved = wsg.resolve_config(wsg.WSG_FP32 if dtype == "fp32" else wsg.WSG_BF16, M, N, K, stages, config)
     log("gemm workload %d %s: %s stages=%d" % (args.workload, w["name"], resolved, stages))
 
@@ -194,6 +195,7 @@ def run(args):
             "M": M, "N": N, "K": K, "stages": stages,
             "tile": [resolved["BM"], resolved["BN"], resolved["BK"]],
             "producer_waves": resolved["producer_waves"], "consumer_waves": resolved["consumer_waves"],
+            "group_k": resolved["group_k"],
             "input": "uniform[-1,1) splitmix64" if dtype == "fp32" else "N(0,1)*0.1 rounded to bf16",
         },
     }
@@ -232,6 +234,18 @@ def run(args):
         for _ in range(3):
             copy_dst.copy_(copy_src)
         torch.cuda.synchronize()
+
+    if args.wait_stats:
+        # one more launch of each kernel with the ring's wait counters on
+        wsg.read_wait_stats()
+        wsg.set_wait_stats(True)
+        gemm()
+        if copy_src is not None:
+            copy()
+        st = wsg.read_wait_stats()
+        wsg.set_wait_stats(False)
+        result["wait_stats"] = {k: dict(v, blocked_frac=round(v["blocked"] / v["waits"], 4) if v["waits"] else None)
+                                for k, v in st.items() if v["waits"]}
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, about %.0f s)" % args.cpu_budget)
@@ -280,6 +294,7 @@ def main():
     p.add_argument("--bk", type=int, default=0)
     p.add_argument("--producers", type=int, default=0)
     p.add_argument("--consumers", type=int, default=0)
+    p.add_argument("--group-k", type=int, default=0, help="consumer k per fragment group (16 or 32)")
     p.add_argument("--no-copy", action="store_true")
     p.add_argument("--copy-tile", type=int, default=0, help="staged copy: bytes per ring slot")
     p.add_argument("--copy-stages", type=int, default=0)
@@ -293,6 +308,8 @@ def main():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after timing, run torch's plain 1 GiB device copy 3 times (for counter calibration)")
     p.add_argument("--sweep", action="store_true")
+    p.add_argument("--wait-stats", action="store_true",
+                   help="after timing, count ring flag waits per role over one launch of each kernel")
     args = p.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run the same "

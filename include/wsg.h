@@ -62,6 +62,7 @@ typedef struct wsg_config {
     int consumer_waves;   /* waves that drain it (GEMM: run the MFMAs; copy: store to dst) */
     int copy_tile_bytes;  /* staged copy: bytes per ring slot (default 65536) */
     int flags;            /* WSG_FLAG_* */
+    int group_k;          /* GEMM consumers: k per fragment group read ahead of the MFMAs (16 or 32) */
 } wsg_config;
 
 /*
@@ -137,6 +138,26 @@ const char *wsg_last_error(void);
  * WSG_ELAUNCH if synchronization failed.
  */
 int wsg_check_device_status(void);
+
+/*
+ * Wait statistics, a diagnostic of the ring handshake: with wsg_set_wait_stats(1)
+ * the calling thread's later launches count, per role, every flag wait, the
+ * waits that found the flag not yet flipped, and the polls those took (each
+ * wave keeps the counts in registers and adds them once at its end). The
+ * pages' steady state, consumers never waiting for data and producers
+ * blocked on free slots, reads directly off these numbers.
+ * wsg_read_wait_stats synchronizes the calling thread's stream, copies the
+ * current device's 16 counters to out[16] and clears them:
+ *   out[0..2]   GEMM consumers, full waits   {waits, blocked, polls}
+ *               (a wait settled by an early read of the flag counts as unblocked)
+ *   out[3..5]   GEMM producers, empty waits  {waits, blocked, polls}
+ *   out[6..8]   copy consumers, full waits
+ *   out[9..11]  copy producers, empty waits
+ *   out[12..15] zero
+ * Counts accumulate over launches and across streams of one device until read.
+ */
+int wsg_set_wait_stats(int enable);
+int wsg_read_wait_stats(uint64_t *out);
 
 /* Library version string. */
 const char *wsg_version(void);

@@ -19,7 +19,8 @@ import os
 __all__ = [
     "WsgError", "Config", "lib", "library_path", "EXPORTS",
     "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "resolve_config",
-    "staged_copy", "staged_copy_ex", "check_device_status", "set_stream", "get_stream",
+    "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
+    "set_stream", "get_stream",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
 ]
 
@@ -40,7 +41,7 @@ WSG_FLAG_NONTEMPORAL = 2
 EXPORTS = (
     "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "wsg_gemm_resolve_config",
     "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
-    "wsg_check_device_status", "wsg_version",
+    "wsg_check_device_status", "wsg_set_wait_stats", "wsg_read_wait_stats", "wsg_version",
 )
 
 
@@ -54,7 +55,7 @@ class Config(ctypes.Structure):
     """struct wsg_config; zero fields mean "default"."""
     _fields_ = [("BM", ctypes.c_int), ("BN", ctypes.c_int), ("BK", ctypes.c_int),
                 ("producer_waves", ctypes.c_int), ("consumer_waves", ctypes.c_int),
-                ("copy_tile_bytes", ctypes.c_int), ("flags", ctypes.c_int)]
+                ("copy_tile_bytes", ctypes.c_int), ("flags", ctypes.c_int), ("group_k", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -82,6 +83,8 @@ def _load() -> ctypes.CDLL:
         "wsg_get_stream": ([], vp),
         "wsg_last_error": ([], ctypes.c_char_p),
         "wsg_check_device_status": ([], ci),
+        "wsg_set_wait_stats": ([ci], ci),
+        "wsg_read_wait_stats": ([ctypes.POINTER(ctypes.c_uint64)], ci),
         "wsg_version": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -227,6 +230,21 @@ def staged_copy_ex(src, dst=None, stages: int = 2, config=None):
     _use_current_stream()
     _raise_on(lib.staged_copy_ex(src.data_ptr(), dst.data_ptr(), nbytes, stages, _config(config)))
     return dst
+
+
+def set_wait_stats(enable: bool) -> None:
+    """Count flag waits per role in this thread's later launches (a diagnostic)."""
+    _raise_on(lib.wsg_set_wait_stats(1 if enable else 0))
+
+
+def read_wait_stats() -> dict:
+    """Synchronize, read and clear the wait counters of the current device."""
+    _use_current_stream()
+    buf = (ctypes.c_uint64 * 16)()
+    _raise_on(lib.wsg_read_wait_stats(buf))
+    v = list(buf)
+    names = ("gemm_consumer_full", "gemm_producer_empty", "copy_consumer_full", "copy_producer_empty")
+    return {n: {"waits": v[3 * i], "blocked": v[3 * i + 1], "polls": v[3 * i + 2]} for i, n in enumerate(names)}
 
 
 def check_device_status() -> None:

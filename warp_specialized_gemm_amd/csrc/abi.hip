@@ -11,10 +11,14 @@
 // address (looked up per device with hipGetSymbolAddress) as an argument.
 __device__ unsigned wsg_status_word;
 
+// Wait statistics (see wsg_read_wait_stats); each GPU holds its own copy.
+__device__ unsigned long long wsg_wait_stats[wsg::kStatWords];
+
 namespace {
 
 thread_local hipStream_t tl_stream = nullptr;
 thread_local std::string tl_err;
+thread_local bool tl_wait_stats = false;
 
 std::mutex g_mu;
 std::vector<wsg::DeviceInfo> g_devs;
@@ -48,9 +52,13 @@ int device_info(wsg::DeviceInfo *out) {
         void *p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(wsg_status_word));
         if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+        void *st = nullptr;
+        e = hipGetSymbolAddress(&st, HIP_SYMBOL(wsg_wait_stats));
+        if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
         d.cu_count = prop.multiProcessorCount;
         d.max_lds = (size_t)lds;
         d.status = static_cast<unsigned *>(p);
+        d.stats = static_cast<unsigned long long *>(st);
         d.device = dev;
     }
     *out = d;
@@ -94,6 +102,7 @@ int gemm_impl(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     rc = device_info(&ctx.dev);
     if (rc != WSG_OK) return rc;
     ctx.stream = tl_stream;
+    ctx.wait_stats = tl_wait_stats;
     wsg::GemmPlan plan;
     std::string err;
     rc = wsg::plan_gemm(dtype, M, N, K, A, B, stages, cfg, ctx.dev, &plan, &err);
@@ -113,6 +122,7 @@ int copy_impl(const void *src, void *dst, size_t bytes, int stages, const wsg_co
     int rc = device_info(&ctx.dev);
     if (rc != WSG_OK) return rc;
     ctx.stream = tl_stream;
+    ctx.wait_stats = tl_wait_stats;
     wsg::CopyPlan plan;
     std::string err;
     rc = wsg::plan_copy(bytes, stages, cfg, ctx.dev, &plan, &err);
@@ -162,6 +172,7 @@ int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stag
     out->consumer_waves = plan.v->CWM * plan.v->CWN;
     out->copy_tile_bytes = 0;
     out->flags = plan.v->dma ? 0 : WSG_FLAG_GENERAL_PRODUCER;
+    out->group_k = plan.v->GK;
     return ok();
 }
 
@@ -197,6 +208,27 @@ int wsg_check_device_status(void) {
         if (word & wsg::kStatusGemm) who += who.empty() ? "gemm" : " and gemm";
         return fail(WSG_ETIMEOUT, "a ring flag wait gave up in " + who + " (protocol fault)");
     }
+    return ok();
+}
+
+int wsg_set_wait_stats(int enable) {
+    tl_wait_stats = enable != 0;
+    return ok();
+}
+
+int wsg_read_wait_stats(uint64_t *out) {
+    if (!out) return fail(WSG_EINVAL, "null output array");
+    wsg::DeviceInfo dev;
+    int rc = device_info(&dev);
+    if (rc != WSG_OK) return rc;
+    hipError_t e = hipStreamSynchronize(tl_stream);
+    if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    unsigned long long buf[wsg::kStatWords] = {};
+    e = hipMemcpy(buf, dev.stats, sizeof buf, hipMemcpyDeviceToHost);
+    const unsigned long long zero[wsg::kStatWords] = {};
+    if (e == hipSuccess) e = hipMemcpy(dev.stats, zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("wait statistics copy: ") + hipGetErrorString(e));
+    for (int i = 0; i < wsg::kStatWords; ++i) out[i] = buf[i];
     return ok();
 }
 

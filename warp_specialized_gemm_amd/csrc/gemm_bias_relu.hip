@@ -10,29 +10,29 @@
 // Slot = t mod S, full-wait parity = (t / S) & 1, empty-wait parity =
 // ((t / S) & 1) ^ 1 (ring.hpp).
 //
-// Producers
-//   A (both dtypes) and B (fp32) go global -> LDS by 16-byte LDS-DMA loads
-//   through buffer resources (no VGPRs; completion by vmcnt), the analogue of
-//   an asynchronous bulk copy. Chunks past M, N or K get an out-of-range
-//   offset, which loads zeros, so consumers never mask. Up to S - 1 tiles stay
-//   in flight. This needs 16-byte aligned rows; other shapes use a
+// Producers (one implementation for both dtypes)
+//   A and B go global -> LDS by 16-byte LDS-DMA loads through buffer
+//   resources (no VGPRs; completion by vmcnt), the analogue of an
+//   asynchronous bulk copy. Chunks past M, N or K get an out-of-range offset,
+//   which loads zeros, so consumers never mask. Up to D = min(S - 1, ...)
+//   tiles stay in flight, and the oldest is published before each wait for a
+//   free slot. This needs 16-byte aligned rows; other shapes use a
 //   register-staged producer with per-element masks and the same slot layout.
-//   B (bf16) must arrive k-contiguous per column for the bf16 MFMA, so the
-//   producer loads 8x8 blocks of B into VGPRs, transposes them with byte
-//   permutes and writes B^T into the slot, one tile ahead of the one it
-//   publishes.
 //
-// Slot layout: A as BM rows of BK elements, B^T (bf16) as BN rows of BK
-// elements, both in 16-byte chunks XOR-swizzled within a row so that
-// consecutive rows reading the same chunk index hit distinct banks; B (fp32)
-// as BK rows of BN floats, chunks swizzled by k.
+// Slot layout: A as BM rows of BK elements, 16-byte chunks XOR-swizzled
+// within a row so that consecutive rows reading the same chunk index hit
+// distinct banks; B as BK rows of BN elements (its natural layout), chunks
+// XOR-swizzled by k.
 //
 // Consumers
 //   fp32: v_mfma_f32_16x16x4_f32. Over a 16-deep k group, lane group q
 //   (lanes 16q..16q+15) supplies k = 16g + 4q + j at step j = 0..3, so each
 //   lane's four A values are one 16-byte chunk of its row.
-//   bf16: v_mfma_f32_32x32x16_bf16; lane half h supplies k = 16g + 8h + e,
-//   one 16-byte chunk of A and one of B^T.
+//   bf16: v_mfma_f32_32x32x16_bf16; lane half h supplies k = 16g + 8h + e.
+//   A comes as one 16-byte chunk of its row; B, which is n-contiguous in the
+//   slot, comes through two LDS transpose reads (ds_read_b64_tr_b16): in each
+//   16-lane group, lane i' points at 4 consecutive n of row k0 + i'/4, and
+//   lane i receives rows k0..k0+3 of column n0 + i.
 //   The fragments of the next k group are read while the MFMAs of the current
 //   one run, and a slot is released as soon as its last group is in
 //   registers.
@@ -45,6 +45,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct GemmArgs {
     const unsigned char *A;
@@ -55,6 +57,7 @@ struct GemmArgs {
     int S;
     int tiles_m, tiles_n;
     unsigned *status;
+    unsigned long long *stats;  // wait statistics, or null
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
@@ -89,8 +92,20 @@ __device__ __forceinline__ int row_swizzle(int m) {
     else return m & 7;
 }
 
-// XOR applied to the chunk index of row k of an fp32 B slot (BN/4 >= 16 chunks)
-__device__ __forceinline__ int bk_swizzle(int k) { return ((k >> 2) & 3) << 2; }
+// XOR applied to the chunk index of row k of a B slot (CPR chunks per row).
+// fp32 (CPR >= 16): the four k rows 4 apart that one b32 fragment read spans
+// land in different 64-byte bank groups. bf16: one transpose read has two
+// 16-lane groups (two column halves, 2 chunks each) over the same 4 rows;
+// XOR with 2r + 8(r & 1) (r = k mod 4) puts those 8 (row, chunk) pairs on 8
+// distinct 16-byte positions of a 128-byte span and all 16 pairs of both
+// groups on distinct positions of a 256-byte span. Rows of 8 chunks only get
+// the first part.
+template <int ES, int CPR>
+__device__ __forceinline__ int b_swizzle(int k) {
+    if constexpr (ES == 4) return ((k >> 2) & 3) << 2;
+    else if constexpr (CPR >= 16) return ((k & 3) << 1) | ((k & 1) << 3);
+    else return (k & 3) << 1;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -130,14 +145,15 @@ struct ADma {
 };
 
 // ----------------------------------------------------------------------------
-// fp32 B by LDS-DMA: BK rows x BN floats, chunks swizzled by k.
+// B by LDS-DMA: BK rows x BN elements of ES bytes, chunks swizzled by k.
 // ----------------------------------------------------------------------------
-template <int BN, int BK, int P>
-struct BDmaF32 {
-    static constexpr int CPR = BN / 4;
+template <int BN, int BK, int ES, int P>
+struct BDma {
+    static constexpr int EPC = 16 / ES;
+    static constexpr int CPR = BN / EPC;  // chunks per row
     static constexpr int CHUNKS = BK * CPR;
     static constexpr int NL = CHUNKS / (64 * P);
-    static_assert(CHUNKS % (64 * P) == 0 && CPR >= 16, "B chunks");
+    static_assert(CHUNKS % (64 * P) == 0 && CPR >= (ES == 4 ? 16 : 8), "B chunks");
     uint32_t off[NL];
     int kk[NL];
     bool ok[NL];
@@ -147,17 +163,17 @@ struct BDmaF32 {
         for (int r = 0; r < NL; ++r) {
             const int p = (r * P + wave) * 64 + lane;
             const int k = p / CPR;
-            const int c = (p % CPR) ^ bk_swizzle(k);
-            off[r] = (uint32_t)k * (uint32_t)N * 4u + (uint32_t)c * 16u;
+            const int c = (p % CPR) ^ b_swizzle<ES, CPR>(k);
+            off[r] = (uint32_t)k * (uint32_t)N * ES + (uint32_t)c * 16u;
             kk[r] = k;
-            ok[r] = n0 + 4 * c < N;
+            ok[r] = n0 + EPC * c < N;
         }
     }
     __device__ __forceinline__ void issue(unsigned char *slotB, int wave, const unsigned char *B, int64_t N, int64_t K,
                                           int64_t n0, int64_t k0) const {
-        const int64_t rec = (K * N - k0 * N - n0) * 4;
+        const int64_t rec = (K * N - k0 * N - n0) * ES;
         const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(B + (size_t)(k0 * N + n0) * 4u, (uint32_t)min(rec, (int64_t)0x7FFFFFFF));
+            make_rsrc(B + (size_t)(k0 * N + n0) * ES, (uint32_t)min(rec, (int64_t)0x7FFFFFFF));
 #pragma unroll
         for (int r = 0; r < NL; ++r)
             lds_dma16(rs, slotB + (r * P + wave) * 1024, (ok[r] && k0 + kk[r] < K) ? off[r] : kOobOffset);
@@ -198,83 +214,107 @@ __device__ __forceinline__ void a_general(unsigned char *slotA, int wave, int la
     }
 }
 
-template <int BN, int BK, int P>
-__device__ __forceinline__ void b_general_f32(unsigned char *slotB, int wave, int lane, const float *B, int64_t N,
-                                              int64_t K, int64_t n0, int64_t k0) {
-    constexpr int CPR = BN / 4, NL = BK * CPR / (64 * P);
+template <int BN, int BK, int ES, int P>
+__device__ __forceinline__ void b_general(unsigned char *slotB, int wave, int lane, const unsigned char *B, int64_t N,
+                                          int64_t K, int64_t n0, int64_t k0) {
+    constexpr int EPC = 16 / ES, CPR = BN / EPC, NL = BK * CPR / (64 * P);
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
         const int p = (r * P + wave) * 64 + lane;
         const int k = p / CPR;
-        const int c = (p % CPR) ^ bk_swizzle(k);
-        f32x4 v;
+        const int c = (p % CPR) ^ b_swizzle<ES, CPR>(k);
+        u32x4 v;
+        if constexpr (ES == 4) {
+            const float *Bf = reinterpret_cast<const float *>(B);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t n = n0 + 4 * c + e;
-            v[e] = (k0 + k < K && n < N) ? B[(k0 + k) * N + n] : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                const int64_t n = n0 + 4 * c + e;
+                v[e] = (k0 + k < K && n < N) ? __float_as_uint(Bf[(k0 + k) * N + n]) : 0u;
+            }
+        } else {
+            const uint16_t *Bh = reinterpret_cast<const uint16_t *>(B);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t n = n0 + 8 * c + 2 * e;
+                const uint32_t lo = (k0 + k < K && n < N) ? Bh[(k0 + k) * N + n] : 0u;
+                const uint32_t hi = (k0 + k < K && n + 1 < N) ? Bh[(k0 + k) * N + n + 1] : 0u;
+                v[e] = lo | (hi << 16);
+            }
         }
-        *reinterpret_cast<f32x4 *>(slotB + (size_t)p * 16u) = v;
+        *reinterpret_cast<u32x4 *>(slotB + (size_t)p * 16u) = v;
     }
 }
 
 // ----------------------------------------------------------------------------
-// bf16 B: 8x8 blocks loaded into VGPRs, transposed, written as B^T rows.
+// Producer waves, shared by both kernels.
 // ----------------------------------------------------------------------------
-template <int BN, int BK, int P>
-struct BTransBf16 {
-    static constexpr int NBN = BN / 8, NBK = BK / 8;
-    static constexpr int NBLK = NBN * NBK;
-    static constexpr int NBL = (NBLK + 64 * P - 1) / (64 * P);  // blocks per lane (the last may be idle)
-    static constexpr int QPR = BK / 8;
-    u32x4 v[NBL][8];
-
-    // fast: every row chunk is 16-byte aligned (N % 8 == 0 and B 16-byte aligned)
-    template <bool FAST>
-    __device__ __forceinline__ void load(int wave, int lane, const uint16_t *B, int64_t N, int64_t K, int64_t n0,
-                                         int64_t k0) {
-#pragma unroll
-        for (int b = 0; b < NBL; ++b) {
-            const int blk = (b * P + wave) * 64 + lane;
-            const int kb = blk / NBN, nb = blk % NBN;
-            const int64_t n = blk < NBLK ? n0 + 8 * nb : N;  // idle lanes load nothing
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int64_t k = k0 + 8 * kb + r;
-                if (FAST) {
-                    if (k < K && n < N)
-                        v[b][r] = *reinterpret_cast<const u32x4 *>(B + k * N + n);
-                    else
-                        v[b][r] = u32x4{0u, 0u, 0u, 0u};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = (k < K && n + 2 * e < N) ? B[k * N + n + 2 * e] : 0u;
-                        const uint32_t hi = (k < K && n + 2 * e + 1 < N) ? B[k * N + n + 2 * e + 1] : 0u;
-                        v[b][r][e] = lo | (hi << 16);
-                    }
-                }
+template <int BM, int BN, int BK, int ES, int P, int NCW, bool DMA>
+__device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, uint32_t fb, int wave, int lane,
+                                        int64_t m0, int64_t n0, int T) {
+    constexpr int A_BYTES = BM * BK * ES, SLOT = A_BYTES + BK * BN * ES;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int S = a.S;
+    const int rows_valid = (int)min((int64_t)BM, M - m0);
+    const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * ES;
+    int s = 0;
+    uint32_t lap = 0;
+    WaitTally tally;
+    if constexpr (DMA) {
+        using AD = ADma<BM, BK, ES, P>;
+        using BD = BDma<BN, BK, ES, P>;
+        constexpr int NL = AD::NL + BD::NL;
+        static_assert(NL <= 63, "one tile's loads must fit vmcnt");
+        AD ad;
+        BD bd;
+        ad.init(wave, lane, K, rows_valid);
+        bd.init(wave, lane, N, n0);
+        // Up to D tiles in flight. The oldest is completed and published
+        // before the wait for the next free slot, so a full signal never
+        // waits on an empty one (the producer spends the steady state of a
+        // compute-bound kernel blocked on empty slots).
+        const int D = max(1, min(S - 1, 63 / NL));
+        int inflight = 0, ps = 0;  // tiles issued but not published; slot of the oldest
+        for (int t = 0; t < T; ++t) {
+            if (inflight == D) {
+                wait_vmcnt_dyn((D - 1) * NL);
+                flag_arrive(full_flag(fb, ps));
+                if (++ps == S) ps = 0;
+                --inflight;
+            }
+            if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+            const int64_t k0 = (int64_t)t * BK;
+            unsigned char *slot = ring + (size_t)s * SLOT;
+            ad.issue(slot, wave, A_rows, rows_valid, K, k0);
+            bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
+            ++inflight;
+            if (++s == S) {
+                s = 0;
+                ++lap;
+            }
+        }
+        while (inflight > 0) {
+            wait_vmcnt_dyn((inflight - 1) * NL);
+            flag_arrive(full_flag(fb, ps));
+            if (++ps == S) ps = 0;
+            --inflight;
+        }
+    } else {
+        for (int t = 0; t < T; ++t) {
+            if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+            const int64_t k0 = (int64_t)t * BK;
+            unsigned char *slot = ring + (size_t)s * SLOT;
+            a_general<BM, BK, ES, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
+            b_general<BN, BK, ES, P>(slot + A_BYTES, wave, lane, a.B, N, K, n0, k0);
+            wait_lgkm0();
+            flag_arrive(full_flag(fb, s));
+            if (++s == S) {
+                s = 0;
+                ++lap;
             }
         }
     }
-    __device__ __forceinline__ void store(unsigned char *slotB, int wave, int lane) const {
-#pragma unroll
-        for (int b = 0; b < NBL; ++b) {
-            const int blk = (b * P + wave) * 64 + lane;
-            const int kb = blk / NBN, nb = blk % NBN;
-            if (blk >= NBLK) continue;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                // column c of the block: k pairs (2d, 2d+1) of element c
-                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 o;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(v[b][2 * d + 1][c >> 1], v[b][2 * d][c >> 1], sel);
-                const int nrow = 8 * nb + c;
-                *reinterpret_cast<u32x4 *>(slotB + nrow * QPR * 16 + ((kb ^ row_swizzle<QPR>(nrow)) << 4)) = o;
-            }
-        }
-    }
-};
+    publish_tally(a.stats ? a.stats + kStatGemmProducer : nullptr, tally);
+}
 
 // ----------------------------------------------------------------------------
 // Consumer walk over the ring, shared by both kernels. The K loop is cut into
@@ -287,7 +327,7 @@ struct BTransBf16 {
 // ----------------------------------------------------------------------------
 template <int KG, int P, typename Frag, typename Read, typename Mma>
 __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, int slot_bytes, uint32_t fb,
-                                             unsigned *status, Read read, Mma mma) {
+                                             unsigned *status, WaitTally &tally, Read read, Mma mma) {
     const uint32_t *flagp = reinterpret_cast<const uint32_t *>(ring - kFlagBytes);
     const int U = T * KG;
     if (U == 0) return true;
@@ -296,7 +336,7 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
     uint32_t rlap = 0;
     int cs = 0;          // slot being consumed
     uint32_t peek = 0;   // early value of the next tile's full flag
-    if (!flag_wait<P>(full_flag(fb, 0), 0u, status, kStatusGemm)) return false;
+    if (!flag_wait<P>(full_flag(fb, 0), 0u, status, kStatusGemm, tally)) return false;
     read(f0, ring, 0);
     if (KG == 1 && U > 1) peek = flag_peek(flagp + (S > 1 ? 1 : 0));
     bool alive = true;
@@ -314,10 +354,12 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
                     ++rlap;
                 }
                 if (phase_of<P>(__builtin_amdgcn_readfirstlane(peek)) == (rlap & 1u)) {
-                    if (!flag_wait<P>(full_flag(fb, rs), rlap & 1u, status, kStatusGemm)) {
+                    if (!flag_wait<P>(full_flag(fb, rs), rlap & 1u, status, kStatusGemm, tally)) {
                         alive = false;
                         return;
                     }
+                } else {
+                    ++tally.waits;  // satisfied by the early read
                 }
                 asm volatile("" ::: "memory");
             }
@@ -344,11 +386,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     constexpr int QPR = BK / 4;
     constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4, SLOT = A_BYTES + B_BYTES;
     constexpr int KG = BK / 16;
-    using AD = ADma<BM, BK, 4, P>;
-    using BD = BDmaF32<BN, BK, P>;
-    constexpr int NL = AD::NL + BD::NL;
     static_assert(BK % 16 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
-    static_assert(NL <= 63, "one tile's loads must fit vmcnt");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *ring = lds + kFlagBytes;
@@ -367,62 +405,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     const int S = a.S;
 
     if (wave < P) {
-        // ================= producer =================
-        const int rows_valid = (int)min((int64_t)BM, M - m0);
-        const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * 4u;
-        int s = 0;
-        uint32_t lap = 0;
-        if constexpr (DMA) {
-            AD ad;
-            BD bd;
-            ad.init(wave, lane, K, rows_valid);
-            bd.init(wave, lane, N, n0);
-            // Up to D tiles in flight. The oldest is completed and published
-            // before the wait for the next free slot, so a full signal never
-            // waits on an empty one (the producer spends the steady state of a
-            // compute-bound kernel blocked on empty slots).
-            const int D = max(1, min(S - 1, 63 / NL));
-            int inflight = 0, ps = 0;  // tiles issued but not published; slot of the oldest
-            for (int t = 0; t < T; ++t) {
-                if (inflight == D) {
-                    wait_vmcnt_dyn((D - 1) * NL);
-                    flag_arrive(full_flag(fb, ps));
-                    if (++ps == S) ps = 0;
-                    --inflight;
-                }
-                if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
-                const int64_t k0 = (int64_t)t * BK;
-                unsigned char *slot = ring + (size_t)s * SLOT;
-                ad.issue(slot, wave, A_rows, rows_valid, K, k0);
-                bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
-                ++inflight;
-                if (++s == S) {
-                    s = 0;
-                    ++lap;
-                }
-            }
-            while (inflight > 0) {
-                wait_vmcnt_dyn((inflight - 1) * NL);
-                flag_arrive(full_flag(fb, ps));
-                if (++ps == S) ps = 0;
-                --inflight;
-            }
-        } else {
-            for (int t = 0; t < T; ++t) {
-                if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
-                const int64_t k0 = (int64_t)t * BK;
-                unsigned char *slot = ring + (size_t)s * SLOT;
-                a_general<BM, BK, 4, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
-                b_general_f32<BN, BK, P>(slot + A_BYTES, wave, lane, reinterpret_cast<const float *>(a.B), N, K, n0,
-                                         k0);
-                wait_lgkm0();
-                flag_arrive(full_flag(fb, s));
-                if (++s == S) {
-                    s = 0;
-                    ++lap;
-                }
-            }
-        }
+        produce<BM, BN, BK, 4, P, NCW, DMA>(a, ring, fb, wave, lane, m0, n0, T);
         return;
     }
 
@@ -461,7 +444,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
         for (int jj = 0; jj < 4; ++jj) {
             const int k = 16 * g + 4 * q + jj;
             const unsigned char *row = slotB + k * BN * 4 + b_sub;
-            const int sw = bk_swizzle(k);
+            const int sw = b_swizzle<4, BN / 4>(k);
 #pragma unroll
             for (int j = 0; j < FN; ++j) f.b[j][jj] = *reinterpret_cast<const float *>(row + ((b_chunk[j] ^ sw) << 4));
         }
@@ -476,7 +459,9 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[i][jj], f.b[j][jj], acc[i][j], 0, 0, 0);
     };
 
-    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, read, mma)) return;
+    WaitTally tally;
+    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, tally, read, mma)) return;
+    publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
 
     // epilogue: C = relu(acc + bias[n]); lane (li, q) holds column li and rows
     // 4q + r of each 16x16 block
@@ -515,17 +500,18 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
 // ----------------------------------------------------------------------------
 // bf16 kernel
 // ----------------------------------------------------------------------------
-template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA>
+// GK: k per fragment group (16 or 32). A deeper group gives each consumer
+// step more MFMA work to hide the next group's LDS reads behind.
+template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA, int GK>
 __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArgs a) {
     constexpr int NCW = CWM * CWN;
     constexpr int WTM = BM / CWM, WTN = BN / CWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int QPR = BK / 8;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, SLOT = A_BYTES + B_BYTES;
-    constexpr int KG = BK / 16;
-    using AD = ADma<BM, BK, 2, P>;
-    using BT = BTransBf16<BN, BK, P>;
-    static_assert(BK % 16 == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
+    constexpr int GS = GK / 16;  // 16-deep MFMA steps per group
+    constexpr int KG = BK / GK;
+    static_assert(BK % GK == 0 && (GK == 16 || GK == 32) && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *ring = lds + kFlagBytes;
@@ -544,48 +530,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
     const int S = a.S;
 
     if (wave < P) {
-        // ================= producer =================
-        // Tile t - 1 is transposed and published before the wait for tile t's
-        // slot, then tile t's loads are issued: they land while the producer
-        // waits for the next free slot, and no full signal waits on an empty
-        // one.
-        const int rows_valid = (int)min((int64_t)BM, M - m0);
-        const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * 2u;
-        const uint16_t *B = reinterpret_cast<const uint16_t *>(a.B);
-        AD ad;
-        if constexpr (DMA) ad.init(wave, lane, K, rows_valid);
-        BT bt;
-        auto issue = [&](int t, int s) {
-            const int64_t k0 = (int64_t)t * BK;
-            unsigned char *slot = ring + (size_t)s * SLOT;
-            if constexpr (DMA) {
-                ad.issue(slot, wave, A_rows, rows_valid, K, k0);
-                bt.template load<true>(wave, lane, B, N, K, n0, k0);
-            } else {
-                a_general<BM, BK, 2, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
-                bt.template load<false>(wave, lane, B, N, K, n0, k0);
-            }
-        };
-        auto publish = [&](int s) {
-            wait_vmcnt<0>();  // only this tile's loads are outstanding
-            bt.store(ring + (size_t)s * SLOT + A_BYTES, wave, lane);
-            wait_lgkm0();
-            flag_arrive(full_flag(fb, s));
-        };
-        int s = 0;
-        uint32_t lap = 0;
-        int ps = 0;  // slot of the tile awaiting publication
-        for (int t = 0; t < T; ++t) {
-            if (t > 0) publish(ps);
-            if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm)) return;
-            issue(t, s);
-            ps = s;
-            if (++s == S) {
-                s = 0;
-                ++lap;
-            }
-        }
-        if (T > 0) publish(ps);
+        produce<BM, BN, BK, 2, P, NCW, DMA>(a, ring, fb, wave, lane, m0, n0, T);
         return;
     }
 
@@ -601,39 +546,65 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    int a_off[FM], a_swz[FM], b_off[FN], b_swz[FN];
+    int a_off[FM], a_swz[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int row = wr * WTM + 32 * i + li;
         a_off[i] = row * QPR * 16;
         a_swz[i] = row_swizzle<QPR>(row);
     }
+    // B: in 16-lane group g16 = lane / 16 (k half h = g16 / 2, column half
+    // g16 % 2), lane i' = lane % 16 points at columns 4 * (i' % 4) .. + 3 of k
+    // row 16 g + 8 h + 4 r + i' / 4 (r = 0, 1: the two halves of the lane's 8
+    // k values); the transpose read hands lane i' its column's 4 rows.
+    const int ip = lane & 15;
+    const int b_row = (8 * h + (ip >> 2)) * BN * 2;
+    const int b_sw = b_swizzle<2, BN / 8>(ip >> 2);  // k = 16g + 8h + 4r + ip/4, so k mod 4 = ip/4
+    int b_col[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int row = wc * WTN + 32 * j + li;
-        b_off[j] = A_BYTES + row * QPR * 16;
-        b_swz[j] = row_swizzle<QPR>(row);
+        const int n = wc * WTN + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (ip & 3);
+        b_col[j] = (((n >> 3) ^ b_sw) << 4) + 8 * (ip & 1);
     }
+    // The two halves of a B fragment stay separate until the MFMA that uses
+    // them, so joining them (if the register allocator needs a copy) happens
+    // after the reads have landed, not while they are in flight.
     struct Frag {
-        bf16x8 a[FM];
-        bf16x8 b[FN];
+        bf16x8 a[GS][FM];
+        v4i16 b_lo[GS][FN], b_hi[GS][FN];
     };
     auto read = [&](Frag &f, const unsigned char *slot, int g) {
-        const int c = 2 * g + h;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(slot + a_off[i] + ((c ^ a_swz[i]) << 4));
+        for (int ks = 0; ks < GS; ++ks) {
+            const int step = g * GS + ks;
+            const int c = 2 * step + h;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(slot + b_off[j] + ((c ^ b_swz[j]) << 4));
+            for (int i = 0; i < FM; ++i)
+                f.a[ks][i] = *reinterpret_cast<const bf16x8 *>(slot + a_off[i] + ((c ^ a_swz[i]) << 4));
+            const unsigned char *slotB = slot + A_BYTES + b_row + 16 * step * BN * 2;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                f.b_lo[ks][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(slotB + b_col[j]));
+                f.b_hi[ks][j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(slotB + 4 * BN * 2 + b_col[j]));
+            }
+        }
     };
     auto mma = [&](const Frag &f) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int ks = 0; ks < GS; ++ks)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < FN; ++j) {
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(f.b_lo[ks][j], f.b_hi[ks][j], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], b, acc[i][j], 0, 0, 0);
+            }
     };
 
-    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, read, mma)) return;
+    WaitTally tally;
+    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, tally, read, mma)) return;
+    publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
 
     // epilogue: lane (li, h) holds column li of each 32x32 block and rows
     // 8*(r/4) + 4*h + (r%4) of its 16 registers
@@ -673,11 +644,11 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
 namespace {
 
 #define WSG_F32(BM, BN, BK, P, CWM, CWN, DMA)                                                              \
-    {WSG_FP32, BM, BN, BK, P, CWM, CWN, DMA,                                                               \
+    {WSG_FP32, BM, BN, BK, P, CWM, CWN, DMA, 16,                                                           \
      reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA>)}
-#define WSG_BF(BM, BN, BK, P, CWM, CWN, DMA)                                                               \
-    {WSG_BF16, BM, BN, BK, P, CWM, CWN, DMA,                                                               \
-     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA>)}
+#define WSG_BF(BM, BN, BK, P, CWM, CWN, DMA, GK)                                                           \
+    {WSG_BF16, BM, BN, BK, P, CWM, CWN, DMA, GK,                                                           \
+     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK>)}
 
 // When the caller leaves fields at 0, the first variant (in this order) whose
 // tile matches the size class and whose ring fits in LDS wins.
@@ -688,10 +659,12 @@ const GemmVariant kGemmVariants[] = {
     WSG_F32(64, 64, 16, 1, 2, 2, true),    WSG_F32(256, 128, 32, 1, 4, 2, true),
     WSG_F32(256, 128, 16, 1, 4, 2, true),  WSG_F32(256, 128, 16, 2, 4, 2, false),
     WSG_F32(128, 128, 16, 1, 2, 2, false), WSG_F32(64, 64, 16, 1, 2, 2, false),
-    WSG_BF(256, 128, 64, 2, 2, 2, true),   WSG_BF(256, 128, 32, 1, 2, 2, true),
-    WSG_BF(128, 128, 32, 1, 2, 2, true),   WSG_BF(64, 64, 32, 1, 2, 2, true),
-    WSG_BF(256, 128, 32, 1, 2, 2, false),  WSG_BF(128, 128, 32, 1, 2, 2, false),
-    WSG_BF(64, 64, 32, 1, 2, 2, false),
+    WSG_BF(256, 128, 64, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 2, 2, 2, true, 16),
+    WSG_BF(256, 128, 64, 1, 2, 2, true, 32),  WSG_BF(256, 128, 32, 1, 2, 2, true, 32),
+    WSG_BF(256, 128, 32, 1, 2, 2, true, 16),
+    WSG_BF(128, 128, 64, 1, 2, 2, true, 32),  WSG_BF(128, 128, 32, 1, 2, 2, true, 16),
+    WSG_BF(64, 64, 32, 1, 2, 2, true, 16),    WSG_BF(256, 128, 32, 1, 2, 2, false, 32),
+    WSG_BF(128, 128, 32, 1, 2, 2, false, 16), WSG_BF(64, 64, 32, 1, 2, 2, false, 16),
 };
 
 }  // namespace
@@ -710,6 +683,7 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     int BM = cfg && cfg->BM ? cfg->BM : 0, BN = cfg && cfg->BN ? cfg->BN : 0, BK = cfg && cfg->BK ? cfg->BK : 0;
     int P = cfg && cfg->producer_waves ? cfg->producer_waves : 0;
     int CW = cfg && cfg->consumer_waves ? cfg->consumer_waves : 0;
+    int GK = cfg && cfg->group_k ? cfg->group_k : 0;
     bool force_general = cfg && (cfg->flags & WSG_FLAG_GENERAL_PRODUCER);
     if (!BM && !BN && !BK) {
         // default tile by problem size: small problems need more workgroups
@@ -738,7 +712,7 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
         for (const GemmVariant &v : kGemmVariants) {
             if (v.dtype != dtype || v.dma != want_dma) continue;
             if ((BM && v.BM != BM) || (BN && v.BN != BN) || (BK && v.BK != BK)) continue;
-            if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW)) continue;
+            if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW) || (GK && v.GK != GK)) continue;
             if (want_dma && ((int64_t)v.BM * K * esz >= 0x7FFFFFFF || (int64_t)v.BK * N * esz >= 0x7FFFFFFF))
                 continue;
             const size_t need = (size_t)kFlagBytes + (size_t)stages * (size_t)(v.BM * v.BK + v.BK * v.BN) * esz;
@@ -796,6 +770,7 @@ int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N
     args.tiles_m = (int)plan.tiles_m;
     args.tiles_n = (int)plan.tiles_n;
     args.status = ctx.dev.status;
+    args.stats = ctx.wait_stats ? ctx.dev.stats : nullptr;
     const int threads = (plan.v->P + plan.v->CWM * plan.v->CWN) * 64;
     hipError_t e =
         hipFuncSetAttribute(plan.v->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);

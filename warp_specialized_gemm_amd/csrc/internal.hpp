@@ -17,11 +17,13 @@ struct DeviceInfo {
     int cu_count = 0;
     size_t max_lds = 0;  // bytes of LDS one workgroup may allocate
     unsigned *status = nullptr;  // device address of the status word
+    unsigned long long *stats = nullptr;  // device address of the wait statistics
 };
 
 struct LaunchCtx {
     hipStream_t stream = nullptr;
     DeviceInfo dev;
+    bool wait_stats = false;  // pass dev.stats to the kernels
 };
 
 // One compiled GEMM variant.
@@ -31,6 +33,7 @@ struct GemmVariant {
     int P;        // producer waves
     int CWM, CWN; // consumer wave grid
     bool dma;     // LDS-DMA producer (aligned shapes) or register-staged producer (any shape)
+    int GK;       // consumer k per fragment group
     const void *kernel;
 };
 

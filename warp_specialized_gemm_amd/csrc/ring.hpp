@@ -41,6 +41,14 @@ constexpr uint32_t kSpinLimit = 1u << 25;  // about a second of polling
 constexpr int kFlagBytes = 256;            // LDS bytes reserved for flags at offset 0
 constexpr int kMaxStages = 32;             // full[32] + empty[32] words fit in kFlagBytes
 
+// wait statistics layout (unsigned long long[16]): each block of three is
+// {waits, waits that found the flag unflipped, polls}
+constexpr int kStatGemmConsumer = 0;  // full waits of GEMM consumers (early flag reads count as waits)
+constexpr int kStatGemmProducer = 3;  // empty waits of GEMM producers
+constexpr int kStatCopyConsumer = 6;
+constexpr int kStatCopyProducer = 9;
+constexpr int kStatWords = 16;
+
 // device status word bits
 constexpr unsigned kStatusTimeout = 1u;
 constexpr unsigned kStatusCopy = 2u;
@@ -74,21 +82,42 @@ __device__ __forceinline__ uint32_t phase_of(uint32_t word) {
     return (word >> log2_arrivals<E>()) & 1u;
 }
 
+// Per-wave count of flag waits, kept in registers: how many waits there
+// were, how many found the flag not yet flipped, and how many polls those
+// took. Written out only when the host asks for wait statistics.
+struct WaitTally {
+    uint32_t waits = 0, blocked = 0, polls = 0;
+};
+
 // Proceed once the phase bit differs from `parity`, i.e. once the phase of
 // that parity has completed. Returns false (after recording the timeout)
 // when the wait gives up.
 template <int E>
-__device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsigned *status, unsigned who) {
+__device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsigned *status, unsigned who,
+                                          WaitTally &tally) {
     uint32_t spins = 0;
+    ++tally.waits;
     while (true) {
         const uint32_t v = __builtin_amdgcn_readfirstlane(flag_load(addr));
-        if (phase_of<E>(v) != parity) return true;
+        if (phase_of<E>(v) != parity) {
+            tally.blocked += spins != 0;
+            tally.polls += spins;
+            return true;
+        }
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
             if ((threadIdx.x & 63) == 0) atomicOr(status, kStatusTimeout | who);
             return false;
         }
     }
+}
+
+// Add a wave's tally to stats[0..2] (once per wave, at its end).
+__device__ __forceinline__ void publish_tally(unsigned long long *stats, const WaitTally &t) {
+    if (!stats || (threadIdx.x & 63) != 0) return;
+    atomicAdd(stats + 0, (unsigned long long)t.waits);
+    atomicAdd(stats + 1, (unsigned long long)t.blocked);
+    atomicAdd(stats + 2, (unsigned long long)t.polls);
 }
 
 // One arrival of the calling wave (lane 0 adds 1). The caller has already

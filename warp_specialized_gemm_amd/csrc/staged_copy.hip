@@ -25,7 +25,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <int P, int C, int TILE, bool NT>
 __global__ void __launch_bounds__((P + C) * 64)
     staged_copy_kernel(const unsigned char *__restrict__ src, unsigned char *__restrict__ dst, uint64_t bytes,
-                       uint64_t ntiles, int S, unsigned *status) {
+                       uint64_t ntiles, int S, unsigned *status, unsigned long long *stats) {
     static_assert(TILE % (P * 1024) == 0 && TILE % (C * 1024) == 0, "tile must split into 1 KiB wave chunks");
     constexpr int NL = TILE / (P * 1024);  // LDS-DMA loads per producer wave per tile
     constexpr int NC = TILE / (C * 1024);  // 16-byte reads per consumer lane per tile
@@ -45,6 +45,7 @@ __global__ void __launch_bounds__((P + C) * 64)
     if (g >= ntiles) return;
     const int64_t nloc = (int64_t)((ntiles - g + G - 1) / G);  // tiles of this workgroup
 
+    WaitTally tally;
     if (wave < P) {
         // ---------------- producer ----------------
         // Up to D tiles in flight; the oldest is completed and published
@@ -76,7 +77,7 @@ __global__ void __launch_bounds__((P + C) * 64)
                 finish(j - D);
                 --inflight;
             }
-            if (!flag_wait<C>(empty_flag(fb, s), (lap & 1u) ^ 1u, status, kStatusCopy)) return;
+            if (!flag_wait<C>(empty_flag(fb, s), (lap & 1u) ^ 1u, status, kStatusCopy, tally)) return;
             const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
             const uint64_t valid = min((uint64_t)TILE, bytes - base);
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + base, (uint32_t)(valid & ~(uint64_t)15));
@@ -96,13 +97,14 @@ __global__ void __launch_bounds__((P + C) * 64)
             wait_vmcnt_dyn((int)(nloc - 1 - j) * NL);
             finish(j);
         }
+        publish_tally(stats ? stats + kStatCopyProducer : nullptr, tally);
     } else {
         // ---------------- consumer ----------------
         const int cw = wave - P;
         int s = 0;
         uint32_t lap = 0;
         for (int64_t j = 0; j < nloc; ++j) {
-            if (!flag_wait<P>(full_flag(fb, s), lap & 1u, status, kStatusCopy)) return;
+            if (!flag_wait<P>(full_flag(fb, s), lap & 1u, status, kStatusCopy, tally)) return;
             const unsigned char *slot = ring + (size_t)s * TILE;
             uint4 v[NC];
 #pragma unroll
@@ -142,6 +144,7 @@ __global__ void __launch_bounds__((P + C) * 64)
                 ++lap;
             }
         }
+        publish_tally(stats ? stats + kStatCopyConsumer : nullptr, tally);
     }
 }
 
@@ -239,7 +242,8 @@ int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, voi
     uint64_t nb = bytes;
     int S = plan.stages;
     unsigned *status = ctx.dev.status;
-    void *args[] = {&s, &d, &nb, (void *)&ntiles, &S, &status};
+    unsigned long long *stats = ctx.wait_stats ? ctx.dev.stats : nullptr;
+    void *args[] = {&s, &d, &nb, (void *)&ntiles, &S, &status, &stats};
     e = hipLaunchKernel(plan.kernel, dim3((unsigned)grid), dim3(threads), args, plan.lds_bytes, ctx.stream);
     if (e != hipSuccess) {
         *err = std::string("staged_copy launch: ") + hipGetErrorString(e);
