@@ -2,7 +2,7 @@
 """Benchmark of the hot path on one MI355X: prints ONE JSON line.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-one fp32 GEMM + bias + ReLU (M = N = K = 4096, uniform[-1,1), 4-stage ring,
+one fp32 GEMM + bias + ReLU (M = N = K = 4096, uniform[-1,1), 2-stage ring,
 default launch configuration) and one LDS-staged copy of 1 GiB of fp32
 (64 KiB tiles, 2-stage ring). Inputs are generated on the host, copied to
 HBM and resident before timing starts.
@@ -15,6 +15,10 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
   roofline             = the GEMM kernel against the fp32 MFMA peak
   copy_roofline        = the copy kernel against the HBM peak
   cpu_baseline         = the CPU oracle on a bounded sample of the same GEMM
+  homogeneous_baseline = the same GEMM, tile and ring depth on the kernel
+                         without roles (every wave loads, barrier, computes)
+  copy.plain_device_copy = torch's own device-to-device copy of the same
+                         buffers, the bandwidth a plain copy kernel reaches
 Options select other workloads (--workload 4: ragged fp32, --workload 5:
 bf16 8192^3) or a launch configuration (--stages, --bm/--bn/--bk,
 --producers, --consumers); --sweep prints one line per stage/producer point.
@@ -139,10 +143,12 @@ def run(args):
     dtype = w["dtype"]
     stages = args.stages or w["stages"]
     config = None
-    if any(v for v in (args.bm, args.bn, args.bk, args.producers, args.consumers, args.group_k)):
+    if any(v for v in (args.bm, args.bn, args.bk, args.producers, args.consumers, args.group_k, args.homogeneous,
+                       args.flags)):
         config = dict(BM=args.bm or 0, BN=args.bn or 0, BK=args.bk or 0,
                       producer_waves=args.producers or 0, consumer_waves=args.consumers or 0,
-                      group_k=args.group_k or 0)
+                      group_k=args.group_k or 0,
+                      flags=args.flags | (wsg.WSG_FLAG_HOMOGENEOUS if args.homogeneous else 0))
     resolved = wsg.resolve_config(wsg.WSG_FP32 if dtype == "fp32" else wsg.WSG_BF16, M, N, K, stages, config)
     log("gemm workload %d %s: %s stages=%d" % (args.workload, w["name"], resolved, stages))
 
@@ -195,7 +201,7 @@ def run(args):
             "M": M, "N": N, "K": K, "stages": stages,
             "tile": [resolved["BM"], resolved["BN"], resolved["BK"]],
             "producer_waves": resolved["producer_waves"], "consumer_waves": resolved["consumer_waves"],
-            "group_k": resolved["group_k"],
+            "group_k": resolved["group_k"], "homogeneous": bool(resolved["flags"] & wsg.WSG_FLAG_HOMOGENEOUS),
             "input": "uniform[-1,1) splitmix64" if dtype == "fp32" else "N(0,1)*0.1 rounded to bf16",
         },
     }
@@ -207,6 +213,32 @@ def run(args):
                           "frac": round(achieved / peak, 4), "traffic": traffic,
                           "kernel_ms": round(g_kern * 1e3, 4), "kernel_ms_min": round(g_min * 1e3, 4)}
     step_s = g_wall / args.steps
+
+    if not args.homogeneous and not args.no_ablation:
+        # the same GEMM on the kernel without roles: same tile, consumer waves,
+        # fragments and ring depth; every wave loads, a barrier, every wave computes
+        hcfg = dict(BM=resolved["BM"], BN=resolved["BN"], BK=resolved["BK"],
+                    consumer_waves=resolved["consumer_waves"], group_k=resolved["group_k"],
+                    flags=wsg.WSG_FLAG_HOMOGENEOUS)
+        try:
+            dC_h = torch.empty_like(dC)
+            hgemm = lambda: wsg.gemm_bias_relu_ex(dA, dB, dbias, dC_h, stages=stages, config=hcfg)  # noqa: E731
+            for _ in range(args.warmup):
+                hgemm()
+            h_wall, h_kern, h_min = time_region(torch, hgemm, args.steps)
+            wsg.check_device_status()
+            h_ach = flops / h_kern / 1e12
+            result["homogeneous_baseline"] = {
+                "tile": [hcfg["BM"], hcfg["BN"], hcfg["BK"]], "waves": hcfg["consumer_waves"], "stages": stages,
+                "value": round(flops * args.steps / h_wall / 1e12, 3), "unit": "TFLOP/s",
+                "kernel_tflops": round(h_ach, 3), "frac": round(h_ach / peak, 4),
+                "kernel_ms": round(h_kern * 1e3, 4),
+                "specialized_speedup": round(h_kern / g_kern, 4),
+                "bit_identical_to_specialized": bool(torch.equal(dC_h, dC)),
+            }
+            del dC_h
+        except wsg.WsgError as e:
+            result["homogeneous_baseline"] = {"error": str(e)}
 
     if copy_src is not None:
         c_wall, c_kern, c_min = time_region(torch, copy, args.steps)
@@ -223,6 +255,15 @@ def run(args):
                                    "traffic": measured_traffic("copy_1GiB_64KiB", "copy"),
                                    "kernel_ms": round(c_kern * 1e3, 4), "kernel_ms_min": round(c_min * 1e3, 4)}
         step_s += c_wall / args.steps
+        # torch's own device copy of the same buffers, timed the same way: what
+        # a plain (unstaged) copy kernel reaches on this device
+        plain = lambda: copy_dst.copy_(copy_src)  # noqa: E731
+        plain()
+        _, p_kern, _ = time_region(torch, plain, args.steps)
+        result["copy"]["plain_device_copy"] = {"value": round(moved / p_kern / 1e9, 1), "unit": "GB/s",
+                                               "kind": "torch Tensor.copy_ on the device"}
+        result["copy"]["staged_over_plain"] = round(p_kern / c_kern, 4)
+        copy()  # leave the staged copy's output in dst for --check
         if args.check:
             eq = torch.equal(copy_dst, copy_src)
             result["copy"]["bit_exact_vs_source"] = bool(eq)
@@ -262,23 +303,25 @@ def run(args):
 
 def sweep(args):
     """Ring depth S in 2, 3, 4 x 1 or 2 producer waves on the 4096^3 fp32 GEMM
-    (256x128 tiles; each point takes the deepest k tile whose ring fits in LDS)."""
+    (256x128 tiles; each point takes the deepest k tile whose ring fits in LDS),
+    then the kernel without roles at S = 1, 2, 3 on the same tiles."""
     import copy as _copy
     out = []
-    for producers in (1, 2):
-        for stages in (2, 3, 4):
-            a = _copy.copy(args)
-            a.stages, a.producers, a.no_copy, a.no_cpu_baseline = stages, producers, True, True
-            a.bm, a.bn, a.consumers = a.bm or 256, a.bn or 128, a.consumers or 8
-            try:
-                r = run(a)
-                line = {"stages": stages, "producer_waves": producers, "tile": r["config"]["tile"],
-                        "consumer_waves": r["config"]["consumer_waves"], "tflops": r["value"],
-                        "kernel_tflops": r["roofline"]["achieved"], "frac": r["roofline"]["frac"]}
-            except Exception as e:  # an unsupported point is reported, not fatal
-                line = {"stages": stages, "producer_waves": producers, "error": str(e)}
-            print(json.dumps(line), flush=True)
-            out.append(line)
+    points = [(p, s, False) for p in (1, 2) for s in (2, 3, 4)] + [(0, s, True) for s in (1, 2, 3)]
+    for producers, stages, homogeneous in points:
+        a = _copy.copy(args)
+        a.stages, a.producers, a.no_copy, a.no_cpu_baseline = stages, producers, True, True
+        a.homogeneous, a.no_ablation = homogeneous, True
+        a.bm, a.bn, a.consumers = a.bm or 256, a.bn or 128, a.consumers or 8
+        try:
+            r = run(a)
+            line = {"stages": stages, "producer_waves": producers, "homogeneous": homogeneous,
+                    "tile": r["config"]["tile"], "consumer_waves": r["config"]["consumer_waves"],
+                    "tflops": r["value"], "kernel_tflops": r["roofline"]["achieved"], "frac": r["roofline"]["frac"]}
+        except Exception as e:  # an unsupported point is reported, not fatal
+            line = {"stages": stages, "producer_waves": producers, "homogeneous": homogeneous, "error": str(e)}
+        print(json.dumps(line), flush=True)
+        out.append(line)
     return out
 
 
@@ -295,6 +338,8 @@ def main():
     p.add_argument("--producers", type=int, default=0)
     p.add_argument("--consumers", type=int, default=0)
     p.add_argument("--group-k", type=int, default=0, help="consumer k per fragment group (16 or 32)")
+    p.add_argument("--flags", type=int, default=0,
+                   help="GEMM wsg_config.flags bits (1: register-staged producer)")
     p.add_argument("--no-copy", action="store_true")
     p.add_argument("--copy-tile", type=int, default=0, help="staged copy: bytes per ring slot")
     p.add_argument("--copy-stages", type=int, default=0)
@@ -307,6 +352,9 @@ def main():
     p.add_argument("--check", action="store_true", help="also compare the copy's output on the GPU")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after timing, run torch's plain 1 GiB device copy 3 times (for counter calibration)")
+    p.add_argument("--homogeneous", action="store_true",
+                   help="time the GEMM kernel without roles (every wave loads, barrier, computes) instead")
+    p.add_argument("--no-ablation", action="store_true", help="skip the homogeneous_baseline measurement")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--wait-stats", action="store_true",
                    help="after timing, count ring flag waits per role over one launch of each kernel")

@@ -51,6 +51,7 @@ extern "C" {
 /* flags for wsg_config.flags */
 #define WSG_FLAG_GENERAL_PRODUCER 1 /* GEMM: force the register-staged producer (any shape) over the LDS-DMA one */
 #define WSG_FLAG_NONTEMPORAL 2      /* staged copy: streaming (non-temporal) loads and stores */
+#define WSG_FLAG_HOMOGENEOUS 4      /* GEMM: the baseline without roles (see below); producer_waves must be 0 */
 
 /*
  * Launch configuration. A zero field means "choose the default". The
@@ -94,6 +95,17 @@ int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, cons
  */
 int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                       const void *bias, float *C, int stages, const wsg_config *cfg);
+
+/*
+ * WSG_FLAG_HOMOGENEOUS selects the kernel the wave-specialized one is measured
+ * against ([KP] section 1.1): the same tiles, slot layout and consumer
+ * fragments, but no producer waves. Every wave loads its share of each K-tile,
+ * a workgroup barrier publishes the tile, and every wave computes on it.
+ * stages == 1 is that loop as written (load, barrier, compute, barrier);
+ * stages >= 2 loads tile t + S - 1 while tile t is computed, with one barrier
+ * per tile. It needs the LDS-DMA alignment (K and N multiples of 16 bytes,
+ * 16-byte aligned A and B; else WSG_EUNSUPPORTED).
+ */
 
 /*
  * The configuration gemm_bias_relu_ex would launch for these arguments,

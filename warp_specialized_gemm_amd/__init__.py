@@ -22,6 +22,7 @@ __all__ = [
     "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
     "set_stream", "get_stream",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
+    "WSG_FLAG_HOMOGENEOUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,7 @@ WSG_FP32 = 0
 WSG_BF16 = 1
 WSG_FLAG_GENERAL_PRODUCER = 1
 WSG_FLAG_NONTEMPORAL = 2
+WSG_FLAG_HOMOGENEOUS = 4
 
 # every function include/wsg.h declares
 EXPORTS = (

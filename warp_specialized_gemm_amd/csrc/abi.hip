@@ -171,7 +171,7 @@ int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stag
     out->producer_waves = plan.v->P;
     out->consumer_waves = plan.v->CWM * plan.v->CWN;
     out->copy_tile_bytes = 0;
-    out->flags = plan.v->dma ? 0 : WSG_FLAG_GENERAL_PRODUCER;
+    out->flags = (plan.v->dma ? 0 : WSG_FLAG_GENERAL_PRODUCER) | (plan.v->P == 0 ? WSG_FLAG_HOMOGENEOUS : 0);
     out->group_k = plan.v->GK;
     return ok();
 }

@@ -24,7 +24,7 @@
 // distinct banks; B as BK rows of BN elements (its natural layout), chunks
 // XOR-swizzled by k.
 //
-// Consumers
+// Consumers (one wave per SIMD in the default tiles: 2 x 2 waves of 128 x 64)
 //   fp32: v_mfma_f32_16x16x4_f32. Over a 16-deep k group, lane group q
 //   (lanes 16q..16q+15) supplies k = 16g + 4q + j at step j = 0..3, so each
 //   lane's four A values are one 16-byte chunk of its row.
@@ -36,6 +36,15 @@
 //   The fragments of the next k group are read while the MFMAs of the current
 //   one run, and a slot is released as soon as its last group is in
 //   registers.
+//   On gfx950, while a wave streams fp32 MFMAs, LDS reads issued by the other
+//   waves on its SIMD wait until the stream pauses. Two fp32 consumers on a
+//   SIMD would hold back each other's fragment reads, so the fp32 default puts
+//   one consumer (a 128 x 64 wave tile) on each SIMD; the producer's flag polls
+//   still wait behind its SIMD's consumer.
+//
+// The homogeneous kernel (no producer waves; sync_loop below) runs the same
+// consumer fragments and MFMA order with workgroup barriers instead of roles,
+// as the baseline the specialization is measured against.
 #include "internal.hpp"
 #include "ring.hpp"
 
@@ -81,6 +90,14 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     const int rem = L - grp * per_group;
     tm = first_m + rem % gm;
     tn = rem / gm;
+}
+
+// Kernel prologue for the ring's flags: zero the LDS flag words, then the
+// workgroup's first (and the specialized kernels' only) barrier.
+__device__ __forceinline__ LdsFlags init_flags(unsigned char *lds) {
+    if (threadIdx.x < kFlagBytes / 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0u;
+    __syncthreads();
+    return LdsFlags{lds_addr(lds), reinterpret_cast<const uint32_t *>(lds)};
 }
 
 __device__ __forceinline__ float relu_f32(float v) { return (v > 0.0f || v != v) ? v : 0.0f; }
@@ -248,8 +265,8 @@ __device__ __forceinline__ void b_general(unsigned char *slotB, int wave, int la
 // ----------------------------------------------------------------------------
 // Producer waves, shared by both kernels.
 // ----------------------------------------------------------------------------
-template <int BM, int BN, int BK, int ES, int P, int NCW, bool DMA>
-__device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, uint32_t fb, int wave, int lane,
+template <int BM, int BN, int BK, int ES, int P, int NCW, bool DMA, typename Flags>
+__device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, const Flags &fl, int wave, int lane,
                                         int64_t m0, int64_t n0, int T) {
     constexpr int A_BYTES = BM * BK * ES, SLOT = A_BYTES + BK * BN * ES;
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -277,11 +294,11 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
         for (int t = 0; t < T; ++t) {
             if (inflight == D) {
                 wait_vmcnt_dyn((D - 1) * NL);
-                flag_arrive(full_flag(fb, ps));
+                fl.arrive_full(ps);
                 if (++ps == S) ps = 0;
                 --inflight;
             }
-            if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+            if (!fl.template wait_empty<NCW>(s, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
             const int64_t k0 = (int64_t)t * BK;
             unsigned char *slot = ring + (size_t)s * SLOT;
             ad.issue(slot, wave, A_rows, rows_valid, K, k0);
@@ -294,19 +311,19 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
         }
         while (inflight > 0) {
             wait_vmcnt_dyn((inflight - 1) * NL);
-            flag_arrive(full_flag(fb, ps));
+            fl.arrive_full(ps);
             if (++ps == S) ps = 0;
             --inflight;
         }
     } else {
         for (int t = 0; t < T; ++t) {
-            if (!flag_wait<NCW>(empty_flag(fb, s), (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+            if (!fl.template wait_empty<NCW>(s, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
             const int64_t k0 = (int64_t)t * BK;
             unsigned char *slot = ring + (size_t)s * SLOT;
             a_general<BM, BK, ES, P>(slot, wave, lane, a.A, m0, rows_valid, K, k0);
             b_general<BN, BK, ES, P>(slot + A_BYTES, wave, lane, a.B, N, K, n0, k0);
             wait_lgkm0();
-            flag_arrive(full_flag(fb, s));
+            fl.arrive_full(s);
             if (++s == S) {
                 s = 0;
                 ++lap;
@@ -325,10 +342,9 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 // that early value shows the tile unpublished does the wave spin on it.
 // Returns false if a wait gave up.
 // ----------------------------------------------------------------------------
-template <int KG, int P, typename Frag, typename Read, typename Mma>
-__device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, int slot_bytes, uint32_t fb,
+template <int KG, int P, typename Frag, typename Flags, typename Read, typename Mma>
+__device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, int slot_bytes, const Flags &fl,
                                              unsigned *status, WaitTally &tally, Read read, Mma mma) {
-    const uint32_t *flagp = reinterpret_cast<const uint32_t *>(ring - kFlagBytes);
     const int U = T * KG;
     if (U == 0) return true;
     Frag f0, f1;
@@ -336,14 +352,15 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
     uint32_t rlap = 0;
     int cs = 0;          // slot being consumed
     uint32_t peek = 0;   // early value of the next tile's full flag
-    if (!flag_wait<P>(full_flag(fb, 0), 0u, status, kStatusGemm, tally)) return false;
+    if (!fl.template wait_full<P>(0, 0u, status, kStatusGemm, tally)) return false;
     read(f0, ring, 0);
-    if (KG == 1 && U > 1) peek = flag_peek(flagp + (S > 1 ? 1 : 0));
+    if (KG == 1 && U > 1) peek = fl.peek_full(S > 1 ? 1 : 0);
     bool alive = true;
     auto step = [&](int u, Frag &cur, Frag &nxt) {
         wait_lgkm0();  // the reads of group u (and the early flag value) have landed
+        const uint32_t pk = __builtin_amdgcn_readfirstlane(peek);
         if (u % KG == KG - 1) {
-            flag_arrive(empty_flag(fb, cs));
+            fl.arrive_empty(cs);
             if (++cs == S) cs = 0;
         }
         if (u + 1 < U) {
@@ -353,8 +370,8 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
                     rs = 0;
                     ++rlap;
                 }
-                if (phase_of<P>(__builtin_amdgcn_readfirstlane(peek)) == (rlap & 1u)) {
-                    if (!flag_wait<P>(full_flag(fb, rs), rlap & 1u, status, kStatusGemm, tally)) {
+                if (phase_of<P>(pk) == (rlap & 1u)) {
+                    if (!fl.template wait_full<P>(rs, rlap & 1u, status, kStatusGemm, tally)) {
                         alive = false;
                         return;
                     }
@@ -364,7 +381,7 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
                 asm volatile("" ::: "memory");
             }
             read(nxt, ring + (size_t)rs * slot_bytes, rg);
-            if (rg == KG - 1 && u + 1 + KG < U) peek = flag_peek(flagp + (rs + 1 == S ? 0 : rs + 1));
+            if (rg == KG - 1 && u + 1 + KG < U) peek = fl.peek_full(rs + 1 == S ? 0 : rs + 1);
         }
         mma(cur);
     };
@@ -373,6 +390,73 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
         if (alive && u + 1 < U) step(u + 1, f1, f0);
     }
     return alive;
+}
+
+// ----------------------------------------------------------------------------
+// Homogeneous K loop, the baseline that specialization is measured against
+// (pwwt.cn article, section 1.1: every thread loads the next tile into shared
+// memory, a block barrier, every thread computes, a second barrier before the
+// buffer is overwritten). No wave has a role: all NW waves issue their share
+// of each tile's LDS-DMA loads (the same loads and slot layout as the
+// producers above) and all of them compute.
+//   S == 1: that loop as written: load t, wait, barrier, compute t, barrier.
+//   S >= 2: prefetched: tile t + S - 1 goes into the slot of tile t - 1, which
+//           every wave finished reading before the barrier that opened tile t,
+//           so one barrier per tile suffices. A tile's fragments are all read
+//           before the next loads are issued (the compiler orders LDS reads
+//           after outstanding LDS-DMA writes), then its MFMAs run while those
+//           loads fly.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void workgroup_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int BK, int ES, int NW, int KG, typename Frag, typename Read, typename Mma>
+__device__ __forceinline__ void sync_loop(const GemmArgs &a, unsigned char *ring, int wave, int lane, int64_t m0,
+                                          int64_t n0, int T, Read read, Mma mma) {
+    constexpr int A_BYTES = BM * BK * ES, SLOT = A_BYTES + BK * BN * ES;
+    using AD = ADma<BM, BK, ES, NW>;
+    using BD = BDma<BN, BK, ES, NW>;
+    constexpr int NL = AD::NL + BD::NL;
+    static_assert(NL <= 63, "one tile's loads must fit vmcnt");
+    const int64_t N = a.N, K = a.K;
+    const int S = a.S;
+    const int rows_valid = (int)min((int64_t)BM, a.M - m0);
+    const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * ES;
+    AD ad;
+    BD bd;
+    ad.init(wave, lane, K, rows_valid);
+    bd.init(wave, lane, N, n0);
+    // tiles loaded ahead of the one being computed
+    const int ahead = S == 1 ? 1 : min(S - 1, 1 + 63 / NL);
+    int is = 0;  // slot of the next tile to issue
+    auto issue = [&](int t) {
+        unsigned char *slot = ring + (size_t)is * SLOT;
+        ad.issue(slot, wave, A_rows, rows_valid, K, (int64_t)t * BK);
+        bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, (int64_t)t * BK);
+        if (++is == S) is = 0;
+    };
+    for (int t = 0; t < min(ahead, T); ++t) issue(t);
+    Frag f[KG];
+    int cs = 0;  // slot of tile t
+    for (int t = 0; t < T; ++t) {
+        wait_vmcnt_dyn(min(ahead - 1, T - 1 - t) * NL);  // this wave's part of tile t has landed
+        workgroup_barrier();                              // ... and every other wave's
+        const unsigned char *slot = ring + (size_t)cs * SLOT;
+#pragma unroll
+        for (int g = 0; g < KG; ++g) read(f[g], slot, g);
+        wait_lgkm0();
+        if (S > 1 && t + ahead < T) issue(t + ahead);
+#pragma unroll
+        for (int g = 0; g < KG; ++g) mma(f[g]);
+        if (S == 1) {
+            workgroup_barrier();  // every wave is done with the only slot
+            if (t + 1 < T) issue(t + 1);
+        }
+        if (++cs == S) cs = 0;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -390,12 +474,10 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *ring = lds + kFlagBytes;
-    const uint32_t fb = lds_addr(lds);
     const int wave = wave_id();
     const int lane = lane_id();
 
-    if (threadIdx.x < kFlagBytes / 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0u;
-    __syncthreads();  // the only workgroup barrier
+    const LdsFlags fl = init_flags(lds);
 
     int tm, tn;
     tile_coords<(8 * BN / BM > 0 ? 8 * BN / BM : 1)>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -404,9 +486,11 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     const int T = (int)((K + BK - 1) / BK);
     const int S = a.S;
 
-    if (wave < P) {
-        produce<BM, BN, BK, 4, P, NCW, DMA>(a, ring, fb, wave, lane, m0, n0, T);
-        return;
+    if constexpr (P > 0) {
+        if (wave < P) {
+            produce<BM, BN, BK, 4, P, NCW, DMA>(a, ring, fl, wave, lane, m0, n0, T);
+            return;
+        }
     }
 
     // ================= consumer =================
@@ -459,9 +543,14 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[i][jj], f.b[j][jj], acc[i][j], 0, 0, 0);
     };
 
-    WaitTally tally;
-    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, tally, read, mma)) return;
-    publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
+    if constexpr (P == 0) {
+        static_assert(DMA, "the homogeneous loop loads by LDS-DMA");
+        sync_loop<BM, BN, BK, 4, NCW, KG, Frag>(a, ring, cw, lane, m0, n0, T, read, mma);
+    } else {
+        WaitTally tally;
+        if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fl, a.status, tally, read, mma)) return;
+        publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
+    }
 
     // epilogue: C = relu(acc + bias[n]); lane (li, q) holds column li and rows
     // 4q + r of each 16x16 block
@@ -469,29 +558,32 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     float *ctile = a.C + m0 * N + n0;
     const int rbase = wr * WTM + 4 * q, cbase = wc * WTN + li;
     const int rows_valid = (int)min((int64_t)BM, M - m0), cols_valid = (int)min((int64_t)BN, N - n0);
+    // all bias loads first: stores count in the same counter, so a bias load
+    // waited for between stores would also wait for every store before it
+    float bv[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bv[j] = cbase + 16 * j < cols_valid ? bias[cbase + 16 * j] : 0.0f;
     if (rows_valid == BM && cols_valid == BN) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = cbase + 16 * j;
-            const float bv = bias[col];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    ctile[(int64_t)(rbase + 16 * i + r) * N + col] = relu_f32(acc[i][j][r] + bv);
+                    ctile[(int64_t)(rbase + 16 * i + r) * N + col] = relu_f32(acc[i][j][r] + bv[j]);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = cbase + 16 * j;
             if (col >= cols_valid) continue;
-            const float bv = bias[col];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = rbase + 16 * i + r;
-                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv);
+                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv[j]);
                 }
         }
     }
@@ -515,12 +607,10 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *ring = lds + kFlagBytes;
-    const uint32_t fb = lds_addr(lds);
     const int wave = wave_id();
     const int lane = lane_id();
 
-    if (threadIdx.x < kFlagBytes / 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0u;
-    __syncthreads();  // the only workgroup barrier
+    const LdsFlags fl = init_flags(lds);
 
     int tm, tn;
     tile_coords<(8 * BN / BM > 0 ? 8 * BN / BM : 1)>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -529,9 +619,11 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
     const int T = (int)((K + BK - 1) / BK);
     const int S = a.S;
 
-    if (wave < P) {
-        produce<BM, BN, BK, 2, P, NCW, DMA>(a, ring, fb, wave, lane, m0, n0, T);
-        return;
+    if constexpr (P > 0) {
+        if (wave < P) {
+            produce<BM, BN, BK, 2, P, NCW, DMA>(a, ring, fl, wave, lane, m0, n0, T);
+            return;
+        }
     }
 
     // ================= consumer =================
@@ -602,9 +694,14 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
             }
     };
 
-    WaitTally tally;
-    if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fb, a.status, tally, read, mma)) return;
-    publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
+    if constexpr (P == 0) {
+        static_assert(DMA, "the homogeneous loop loads by LDS-DMA");
+        sync_loop<BM, BN, BK, 2, NCW, KG, Frag>(a, ring, cw, lane, m0, n0, T, read, mma);
+    } else {
+        WaitTally tally;
+        if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fl, a.status, tally, read, mma)) return;
+        publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
+    }
 
     // epilogue: lane (li, h) holds column li of each 32x32 block and rows
     // 8*(r/4) + 4*h + (r%4) of its 16 registers
@@ -612,30 +709,31 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
     float *ctile = a.C + m0 * N + n0;
     const int rbase = wr * WTM + 4 * h, cbase = wc * WTN + li;
     const int rows_valid = (int)min((int64_t)BM, M - m0), cols_valid = (int)min((int64_t)BN, N - n0);
+    float bv[FN];  // all bias loads before the first store, as in the fp32 epilogue
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bv[j] = cbase + 32 * j < cols_valid ? bf16_to_f32(bias[cbase + 32 * j]) : 0.0f;
     if (rows_valid == BM && cols_valid == BN) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = cbase + 32 * j;
-            const float bv = bf16_to_f32(bias[col]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     ctile[(int64_t)(rbase + 32 * i + 8 * (r >> 2) + (r & 3)) * N + col] =
-                        relu_f32(acc[i][j][r] + bv);
+                        relu_f32(acc[i][j][r] + bv[j]);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = cbase + 32 * j;
             if (col >= cols_valid) continue;
-            const float bv = bf16_to_f32(bias[col]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = rbase + 32 * i + 8 * (r >> 2) + (r & 3);
-                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv);
+                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv[j]);
                 }
         }
     }
@@ -653,18 +751,35 @@ namespace {
 // When the caller leaves fields at 0, the first variant (in this order) whose
 // tile matches the size class and whose ring fits in LDS wins.
 const GemmVariant kGemmVariants[] = {
-    WSG_F32(256, 128, 32, 2, 4, 2, true),  WSG_F32(256, 128, 16, 2, 4, 2, true),
+    // fp32, wave-specialized, LDS-DMA producer. One consumer wave per SIMD
+    // first: a second one would stall the first one's LDS reads while it
+    // streams fp32 MFMAs.
+    WSG_F32(256, 128, 32, 2, 2, 2, true),  WSG_F32(256, 128, 16, 2, 2, 2, true),
     WSG_F32(128, 128, 32, 2, 2, 2, true),  WSG_F32(128, 128, 16, 1, 2, 2, true),
-    WSG_F32(128, 128, 16, 2, 2, 2, true),  WSG_F32(128, 256, 16, 2, 2, 4, true),
-    WSG_F32(64, 64, 16, 1, 2, 2, true),    WSG_F32(256, 128, 32, 1, 4, 2, true),
-    WSG_F32(256, 128, 16, 1, 4, 2, true),  WSG_F32(256, 128, 16, 2, 4, 2, false),
-    WSG_F32(128, 128, 16, 1, 2, 2, false), WSG_F32(64, 64, 16, 1, 2, 2, false),
+    WSG_F32(128, 128, 16, 2, 2, 2, true),  WSG_F32(64, 64, 16, 1, 2, 2, true),
+    WSG_F32(256, 128, 32, 1, 2, 2, true),  WSG_F32(256, 128, 32, 2, 4, 2, true),
+    WSG_F32(256, 128, 16, 2, 4, 2, true),  WSG_F32(256, 128, 32, 1, 4, 2, true),
+    WSG_F32(256, 128, 16, 1, 4, 2, true),  WSG_F32(256, 128, 32, 4, 4, 2, true),
+    WSG_F32(128, 256, 16, 2, 2, 4, true),
+    // fp32, register-staged producer (any shape)
+    WSG_F32(256, 128, 16, 2, 4, 2, false), WSG_F32(128, 128, 16, 1, 2, 2, false),
+    WSG_F32(64, 64, 16, 1, 2, 2, false),
+    // fp32, homogeneous (no producer waves)
+    WSG_F32(256, 128, 32, 0, 2, 2, true),  WSG_F32(256, 128, 16, 0, 2, 2, true),
+    WSG_F32(256, 128, 32, 0, 4, 2, true),  WSG_F32(256, 128, 16, 0, 4, 2, true),
+    WSG_F32(128, 128, 32, 0, 2, 2, true),
+    WSG_F32(64, 64, 16, 0, 2, 2, true),
+    // bf16, wave-specialized
     WSG_BF(256, 128, 64, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 2, 2, 2, true, 16),
     WSG_BF(256, 128, 64, 1, 2, 2, true, 32),  WSG_BF(256, 128, 32, 1, 2, 2, true, 32),
     WSG_BF(256, 128, 32, 1, 2, 2, true, 16),
     WSG_BF(128, 128, 64, 1, 2, 2, true, 32),  WSG_BF(128, 128, 32, 1, 2, 2, true, 16),
     WSG_BF(64, 64, 32, 1, 2, 2, true, 16),    WSG_BF(256, 128, 32, 1, 2, 2, false, 32),
     WSG_BF(128, 128, 32, 1, 2, 2, false, 16), WSG_BF(64, 64, 32, 1, 2, 2, false, 16),
+    // bf16, homogeneous
+    WSG_BF(256, 128, 64, 0, 2, 2, true, 32),  WSG_BF(256, 128, 64, 0, 4, 2, true, 32),
+    WSG_BF(256, 128, 32, 0, 2, 2, true, 32),  WSG_BF(128, 128, 32, 0, 2, 2, true, 16),
+    WSG_BF(64, 64, 32, 0, 2, 2, true, 16),
 };
 
 }  // namespace
@@ -684,7 +799,13 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     int P = cfg && cfg->producer_waves ? cfg->producer_waves : 0;
     int CW = cfg && cfg->consumer_waves ? cfg->consumer_waves : 0;
     int GK = cfg && cfg->group_k ? cfg->group_k : 0;
-    bool force_general = cfg && (cfg->flags & WSG_FLAG_GENERAL_PRODUCER);
+    const bool force_general = cfg && (cfg->flags & WSG_FLAG_GENERAL_PRODUCER);
+    const bool homogeneous = cfg && (cfg->flags & WSG_FLAG_HOMOGENEOUS);
+    if (homogeneous && (P || force_general)) {
+        *err = "the homogeneous kernel has no producer waves and loads by LDS-DMA: leave producer_waves 0 and "
+               "WSG_FLAG_GENERAL_PRODUCER clear";
+        return WSG_EINVAL;
+    }
     if (!BM && !BN && !BK) {
         // default tile by problem size: small problems need more workgroups
         const int64_t big = (M + 255) / 256 * ((N + 127) / 128);
@@ -704,13 +825,18 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     const int align_elems = 16 / esz;
     const bool aligned = K % align_elems == 0 && N % align_elems == 0 && ((uintptr_t)A % 16) == 0 &&
                          ((uintptr_t)B % 16) == 0;
+    if (homogeneous && !aligned) {
+        *err = "the homogeneous kernel loads by LDS-DMA: K and N must be multiples of " + std::to_string(align_elems) +
+               " and A and B 16-byte aligned";
+        return WSG_EUNSUPPORTED;
+    }
     const GemmVariant *pick = nullptr;
     bool lds_short = false;
     for (int pass = 0; pass < 2 && !pick; ++pass) {
         const bool want_dma = pass == 0;
         if (want_dma && (force_general || !aligned)) continue;
         for (const GemmVariant &v : kGemmVariants) {
-            if (v.dtype != dtype || v.dma != want_dma) continue;
+            if (v.dtype != dtype || v.dma != want_dma || (v.P == 0) != homogeneous) continue;
             if ((BM && v.BM != BM) || (BN && v.BN != BN) || (BK && v.BK != BK)) continue;
             if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW) || (GK && v.GK != GK)) continue;
             if (want_dma && ((int64_t)v.BM * K * esz >= 0x7FFFFFFF || (int64_t)v.BK * N * esz >= 0x7FFFFFFF))

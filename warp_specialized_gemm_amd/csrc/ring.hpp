@@ -92,13 +92,14 @@ struct WaitTally {
 // Proceed once the phase bit differs from `parity`, i.e. once the phase of
 // that parity has completed. Returns false (after recording the timeout)
 // when the wait gives up.
-template <int E>
-__device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsigned *status, unsigned who,
-                                          WaitTally &tally) {
+// `poll` returns the flag word (wave-uniform).
+template <int E, typename Poll>
+__device__ __forceinline__ bool flag_wait_with(Poll poll, uint32_t parity, unsigned *status, unsigned who,
+                                               WaitTally &tally) {
     uint32_t spins = 0;
     ++tally.waits;
     while (true) {
-        const uint32_t v = __builtin_amdgcn_readfirstlane(flag_load(addr));
+        const uint32_t v = poll();
         if (phase_of<E>(v) != parity) {
             tally.blocked += spins != 0;
             tally.polls += spins;
@@ -110,6 +111,13 @@ __device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsign
             return false;
         }
     }
+}
+
+template <int E>
+__device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsigned *status, unsigned who,
+                                          WaitTally &tally) {
+    return flag_wait_with<E>([&] { return __builtin_amdgcn_readfirstlane(flag_load(addr)); }, parity, status, who,
+                             tally);
 }
 
 // Add a wave's tally to stats[0..2] (once per wave, at its end).
@@ -128,11 +136,30 @@ __device__ __forceinline__ void flag_arrive(uint32_t addr) {
     asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
 }
 
-// Consumer-side early read of a flag word (no LDS-DMA in flight in the
-// calling wave); the compiler waits for it where the value is used.
-__device__ __forceinline__ uint32_t flag_peek(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
+// ---------------------------------------------------------------------------
+// The ring's flag words as the kernels use them: full[s] and empty[s] in the
+// first kFlagBytes of the workgroup's LDS, one ds_* instruction per flag
+// operation.
+// ---------------------------------------------------------------------------
+struct LdsFlags {
+    uint32_t fb;            // LDS address of the flag area
+    const uint32_t *words;  // the same area as a generic pointer, for early reads
+    __device__ void arrive_full(int s) const { flag_arrive(full_flag(fb, s)); }
+    __device__ void arrive_empty(int s) const { flag_arrive(empty_flag(fb, s)); }
+    template <int E>
+    __device__ bool wait_full(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {
+        return flag_wait<E>(full_flag(fb, s), parity, status, who, t);
+    }
+    template <int E>
+    __device__ bool wait_empty(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {
+        return flag_wait<E>(empty_flag(fb, s), parity, status, who, t);
+    }
+    // early read of full[s] by a consumer (which has no LDS-DMA in flight);
+    // the compiler waits for it where the value is used
+    __device__ uint32_t peek_full(int s) const {
+        return __hip_atomic_load(words + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+};
 
 // All of this wave's LDS operations done. The builtin (not inline assembly)
 // lets the compiler's own wait insertion see it, so later uses of registers
