@@ -99,6 +99,10 @@ VARIANTS = [
     dict(BM=256, BN=128, BK=64, producer_waves=2, consumer_waves=4, group_k=32),
     dict(BM=256, BN=128, BK=32, producer_waves=1, consumer_waves=4, group_k=32),
     dict(BM=256, BN=128, BK=64, producer_waves=2, consumer_waves=4, group_k=32),
+    dict(BM=256, BN=128, BK=64, producer_waves=4, consumer_waves=4, group_k=32),
+    dict(BM=256, BN=128, BK=64, producer_waves=4, consumer_waves=4, group_k=16),
+    dict(BM=256, BN=128, BK=32, producer_waves=2, consumer_waves=4, group_k=32),
+    dict(BM=256, BN=128, BK=32, producer_waves=4, consumer_waves=4, group_k=16),
 ]
 
 

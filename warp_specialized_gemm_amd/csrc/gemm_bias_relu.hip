@@ -752,8 +752,10 @@ namespace {
 // tile matches the size class and whose ring fits in LDS wins.
 const GemmVariant kGemmVariants[] = {
     // fp32, wave-specialized, LDS-DMA producer. One consumer wave per SIMD
-    // first: a second one would stall the first one's LDS reads while it
-    // streams fp32 MFMAs.
+    // first (a second one would stall the first one's LDS reads while it
+    // streams fp32 MFMAs), with one producer wave per SIMD: a producer shares
+    // its SIMD with a consumer's MFMA stream, which slows its LDS-DMA issue.
+    WSG_F32(256, 128, 32, 4, 2, 2, true),  WSG_F32(256, 128, 16, 4, 2, 2, true),
     WSG_F32(256, 128, 32, 2, 2, 2, true),  WSG_F32(256, 128, 16, 2, 2, 2, true),
     WSG_F32(128, 128, 32, 2, 2, 2, true),  WSG_F32(128, 128, 16, 1, 2, 2, true),
     WSG_F32(128, 128, 16, 2, 2, 2, true),  WSG_F32(64, 64, 16, 1, 2, 2, true),
@@ -773,6 +775,9 @@ const GemmVariant kGemmVariants[] = {
     WSG_BF(256, 128, 64, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 2, 2, 2, true, 16),
     WSG_BF(256, 128, 64, 1, 2, 2, true, 32),  WSG_BF(256, 128, 32, 1, 2, 2, true, 32),
     WSG_BF(256, 128, 32, 1, 2, 2, true, 16),
+    WSG_BF(256, 128, 64, 4, 2, 2, true, 32),  WSG_BF(256, 128, 32, 4, 2, 2, true, 32),
+    WSG_BF(256, 128, 32, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 4, 2, 2, true, 16),
+    WSG_BF(256, 128, 32, 4, 2, 2, true, 16),  WSG_BF(256, 128, 32, 2, 2, 2, true, 16),
     WSG_BF(128, 128, 64, 1, 2, 2, true, 32),  WSG_BF(128, 128, 32, 1, 2, 2, true, 16),
     WSG_BF(64, 64, 32, 1, 2, 2, true, 16),    WSG_BF(256, 128, 32, 1, 2, 2, false, 32),
     WSG_BF(128, 128, 32, 1, 2, 2, false, 16), WSG_BF(64, 64, 32, 1, 2, 2, false, 16),

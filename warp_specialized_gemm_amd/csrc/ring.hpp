@@ -107,7 +107,7 @@ __device__ __forceinline__ bool flag_wait_with(Poll poll, uint32_t parity, unsig
         }
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
-            if ((threadIdx.x & 63) == 0) atomicOr(status, kStatusTimeout | who);
+            atomicOr(status, kStatusTimeout | who);  // every lane: keeps the loop wave-uniform
             return false;
         }
     }
@@ -128,12 +128,22 @@ __device__ __forceinline__ void publish_tally(unsigned long long *stats, const W
     atomicAdd(stats + 2, (unsigned long long)t.polls);
 }
 
-// One arrival of the calling wave (lane 0 adds 1). The caller has already
+// One arrival of the calling wave: lane 0 adds 1. The caller has already
 // waited for the wave's own LDS writes or reads of the slot; LDS operations
-// of one wave execute in order, so nothing here needs waiting for.
+// of one wave execute in order, so nothing here needs waiting for. The add
+// runs with exec narrowed to lane 0 inside the assembly rather than under a
+// lane test, so the code around it stays wave-uniform and the ring counters
+// stay in scalar registers.
 __device__ __forceinline__ void flag_arrive(uint32_t addr) {
-    if ((threadIdx.x & 63) != 0) return;
-    asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
+    uint64_t saved;
+    asm volatile(
+        "s_mov_b64 %0, exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "ds_add_u32 %1, %2\n\t"
+        "s_mov_b64 exec, %0"
+        : "=&s"(saved)
+        : "v"(addr), "v"(1u)
+        : "memory");
 }
 
 // ---------------------------------------------------------------------------
