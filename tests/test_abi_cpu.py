@@ -105,3 +105,12 @@ def test_config_struct_layout_matches_header(wsg):
     fields = re.findall(r"([A-Za-z_]+)\s*[,;]", body)
     assert fields == [f for f, _ in wsg.Config._fields_]
     assert ctypes.sizeof(wsg.Config) == 4 * len(fields)
+
+
+def test_binding_constants_match_header(wsg):
+    """Every WSG_* constant of the header has the same value in the binding."""
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"^#define\s+(WSG_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", text, flags=re.M))
+    assert {"WSG_OK", "WSG_EINVAL", "WSG_FP32", "WSG_BF16", "WSG_FLAG_HOMOGENEOUS"} <= set(defs)
+    for name, value in defs.items():
+        assert getattr(wsg, name) == int(value), name
