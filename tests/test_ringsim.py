@@ -174,3 +174,25 @@ def test_async_fill_lookahead_beyond_S_deadlocks(S):
 def test_async_fill_negative_controls(variant):
     r = rs.explore(2, 6, 1, 2, variant=variant, lookahead=1)
     assert r.deadlock or r.violation is not None
+
+
+def test_ring_depth_from_measured_latency():
+    """Ring depth from the timed model with the cycle counts measured by
+    per-tile timestamps in the 4096^3 fp32 kernel on MI355X (two producer
+    waves): a tile's loads take L ~ 4,400 cycles from the first issue until
+    they land (issue ~3,650, landing ~720 after the last issue), a consumer
+    computes a tile in c ~ 9,600 cycles and releases the slot when the reads
+    of its last k group have landed, half a tile in (two groups of 16 k per
+    32-deep tile). The model then needs one slot beyond the one in use only
+    if the release came at the end of the compute, and two slots are as fast
+    as three: what the stage sweep measured (S = 2 and 3 within 1%)."""
+    L, c, r = 4400.0, 9600.0, 4800.0
+    assert rs.min_stages(L, c, release_after=r) == 1
+    assert rs.min_stages(L, c) == 2
+    periods = {S: rs.timed(S, 64, L, c, release_after=r).period() for S in (1, 2, 3)}
+    assert periods[2] == pytest.approx(c) and periods[3] == pytest.approx(c)
+    assert periods[1] == pytest.approx(rs.steady_period(1, L, c, release_after=r))
+    # the model has no limit on how fast a producer issues: with one producer
+    # wave (issue ~4x longer, ~11,000 cycles of issuing per tile, more than c)
+    # the kernel is bound by issue throughput, which no ring depth changes
+    # (measured: S = 2 and 3 within 1% there too)
