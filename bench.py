@@ -302,17 +302,18 @@ def run(args):
 
 
 def sweep(args):
-    """Ring depth S in 2, 3, 4 x 1 or 2 producer waves on the 4096^3 fp32 GEMM
-    (256x128 tiles; each point takes the deepest k tile whose ring fits in LDS),
-    then the kernel without roles at S = 1, 2, 3 on the same tiles."""
+    """Ring depth S in 2, 3, 4 x 1, 2 or 4 producer waves on the 4096^3 fp32
+    GEMM (256x128 tiles, 4 consumer waves; each point takes the deepest k tile
+    whose ring fits in LDS), then the kernel without roles at S = 1, 2, 3 on
+    the same tiles. Points with no built kernel are printed with the error."""
     import copy as _copy
     out = []
-    points = [(p, s, False) for p in (1, 2) for s in (2, 3, 4)] + [(0, s, True) for s in (1, 2, 3)]
+    points = [(p, s, False) for p in (1, 2, 4) for s in (2, 3, 4)] + [(0, s, True) for s in (1, 2, 3)]
     for producers, stages, homogeneous in points:
         a = _copy.copy(args)
         a.stages, a.producers, a.no_copy, a.no_cpu_baseline = stages, producers, True, True
         a.homogeneous, a.no_ablation = homogeneous, True
-        a.bm, a.bn, a.consumers = a.bm or 256, a.bn or 128, a.consumers or 8
+        a.bm, a.bn, a.consumers = a.bm or 256, a.bn or 128, a.consumers or 4
         try:
             r = run(a)
             line = {"stages": stages, "producer_waves": producers, "homogeneous": homogeneous,
