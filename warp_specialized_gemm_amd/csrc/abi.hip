@@ -1,7 +1,9 @@
 // abi.hip - the extern "C" entry points declared in include/wsg.h: argument
 // validation, per-device state, the calling thread's stream and last error.
+#include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "internal.hpp"
@@ -65,6 +67,10 @@ int device_info(wsg::DeviceInfo *out) {
     return WSG_OK;
 }
 
+std::mutex g_kernel_mu;
+std::map<std::pair<int, const void *>, bool> g_prepared;
+std::map<std::tuple<int, const void *, int, size_t>, int> g_occupancy;
+
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
     if (!an || !bn) return false;
     uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -72,6 +78,7 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 }
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
+constexpr uint64_t kMaxElems = 1ull << 56;  // per operand: keeps every byte count well inside size_t
 
 int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                   const float *C, int stages) {
@@ -80,6 +87,9 @@ int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, con
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WSG_EUNSUPPORTED, "dimension above 2^31 - 1");
     if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
     if (M == 0 || N == 0) return WSG_OK;
+    if ((uint64_t)M * (uint64_t)K > kMaxElems || (uint64_t)K * (uint64_t)N > kMaxElems ||
+        (uint64_t)M * (uint64_t)N > kMaxElems)
+        return fail(WSG_EUNSUPPORTED, "operand larger than 2^56 elements");
     const size_t esz = dtype == WSG_FP32 ? 4 : 2;
     if (K > 0 && (!A || !B)) return fail(WSG_EINVAL, "null A or B with a nonzero size");
     if (!bias || !C) return fail(WSG_EINVAL, "null bias or C with a nonzero size");
@@ -133,6 +143,35 @@ int copy_impl(const void *src, void *dst, size_t bytes, int stages, const wsg_co
 }
 
 }  // namespace
+
+namespace wsg {
+
+int prepare_kernel(const void *kernel, const DeviceInfo &dev, std::string *err) {
+    std::lock_guard<std::mutex> lock(g_kernel_mu);
+    bool &done = g_prepared[{dev.device, kernel}];
+    if (done) return WSG_OK;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
+    if (e != hipSuccess) {
+        *err = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
+        return WSG_ELAUNCH;
+    }
+    done = true;
+    return WSG_OK;
+}
+
+int blocks_per_cu(const void *kernel, const DeviceInfo &dev, int threads, size_t lds) {
+    std::lock_guard<std::mutex> lock(g_kernel_mu);
+    const auto key = std::make_tuple(dev.device, kernel, threads, lds);
+    auto it = g_occupancy.find(key);
+    if (it != g_occupancy.end()) return it->second;
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
+    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    g_occupancy[key] = per_cu;
+    return per_cu;
+}
+
+}  // namespace wsg
 
 extern "C" {
 

@@ -903,14 +903,10 @@ int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N
     args.status = ctx.dev.status;
     args.stats = ctx.wait_stats ? ctx.dev.stats : nullptr;
     const int threads = (plan.v->P + plan.v->CWM * plan.v->CWN) * 64;
-    hipError_t e =
-        hipFuncSetAttribute(plan.v->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
-    if (e != hipSuccess) {
-        *err = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
-        return WSG_ELAUNCH;
-    }
+    const int rc = prepare_kernel(plan.v->kernel, ctx.dev, err);
+    if (rc != WSG_OK) return rc;
     void *kargs[] = {&args};
-    e = hipLaunchKernel(plan.v->kernel, dim3((unsigned)(plan.tiles_m * plan.tiles_n)), dim3(threads), kargs,
+    hipError_t e = hipLaunchKernel(plan.v->kernel, dim3((unsigned)(plan.tiles_m * plan.tiles_n)), dim3(threads), kargs,
                         plan.lds_bytes, ctx.stream);
     if (e != hipSuccess) {
         *err = std::string("gemm launch: ") + hipGetErrorString(e);

@@ -50,6 +50,14 @@ struct CopyPlan {
     size_t lds_bytes = 0;
 };
 
+// Once per (device, kernel): raise the kernel's dynamic-LDS limit to the
+// device maximum, so that launches need no attribute call of their own.
+int prepare_kernel(const void *kernel, const DeviceInfo &dev, std::string *err);
+
+// Workgroups of `threads` threads and `lds` bytes of LDS one CU holds (at
+// least 1), cached per (device, kernel, threads, lds).
+int blocks_per_cu(const void *kernel, const DeviceInfo &dev, int threads, size_t lds);
+
 // Fill `plan` for the arguments; returns WSG_OK or an error code with `err` set.
 int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, int stages,
               const wsg_config *cfg, const DeviceInfo &dev, GemmPlan *plan, std::string *err);

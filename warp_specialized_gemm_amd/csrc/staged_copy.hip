@@ -227,14 +227,9 @@ int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, voi
     if (bytes == 0) return WSG_OK;
     const uint64_t ntiles = (bytes + (uint64_t)plan.tile - 1) / (uint64_t)plan.tile;
     const int threads = (plan.P + plan.C) * 64;
-    hipError_t e = hipFuncSetAttribute(plan.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds_bytes);
-    if (e != hipSuccess) {
-        *err = std::string("hipFuncSetAttribute: ") + hipGetErrorString(e);
-        return WSG_ELAUNCH;
-    }
-    int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, plan.kernel, threads, plan.lds_bytes);
-    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    const int rc = prepare_kernel(plan.kernel, ctx.dev, err);
+    if (rc != WSG_OK) return rc;
+    const int per_cu = blocks_per_cu(plan.kernel, ctx.dev, threads, plan.lds_bytes);
     uint64_t grid = (uint64_t)ctx.dev.cu_count * (uint64_t)per_cu;
     if (grid > ntiles) grid = ntiles;
     const unsigned char *s = static_cast<const unsigned char *>(src);
@@ -244,7 +239,7 @@ int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, voi
     unsigned *status = ctx.dev.status;
     unsigned long long *stats = ctx.wait_stats ? ctx.dev.stats : nullptr;
     void *args[] = {&s, &d, &nb, (void *)&ntiles, &S, &status, &stats};
-    e = hipLaunchKernel(plan.kernel, dim3((unsigned)grid), dim3(threads), args, plan.lds_bytes, ctx.stream);
+    hipError_t e = hipLaunchKernel(plan.kernel, dim3((unsigned)grid), dim3(threads), args, plan.lds_bytes, ctx.stream);
     if (e != hipSuccess) {
         *err = std::string("staged_copy launch: ") + hipGetErrorString(e);
         return WSG_ELAUNCH;
