@@ -167,6 +167,7 @@ def run(args):
         copy_src = torch.from_numpy(synth.uniform_pm1(synth.seed_for(2, "src"), nel)).to(dev)
         copy_dst = torch.empty_like(copy_src)
         copy_cfg = dict(copy_tile_bytes=args.copy_tile or cw["tile_bytes"], producer_waves=args.copy_producers,
+                        copy_workgroups=args.copy_workgroups,
                         consumer_waves=args.copy_consumers, flags=0 if args.copy_cached else wsg.WSG_FLAG_NONTEMPORAL)
         copy_stages = args.copy_stages or cw["stages"]
         copy = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=copy_stages, config=copy_cfg)  # noqa: E731
@@ -248,6 +249,7 @@ def run(args):
         result["copy"] = {"value": round(moved * args.steps / c_wall / 1e9, 1), "unit": "GB/s",
                           "bytes": nbytes, "tile_bytes": copy_cfg["copy_tile_bytes"], "stages": copy_stages,
                           "producer_waves": args.copy_producers or None, "consumer_waves": args.copy_consumers or None,
+                          "workgroups": args.copy_workgroups or None,
                           "nontemporal": not args.copy_cached}
         c_ach = moved / c_kern / 1e9
         result["copy_roofline"] = {"bound": "hbm", "achieved": round(c_ach, 1), "peak": PEAK_HBM_GBS,
@@ -346,6 +348,7 @@ def main():
     p.add_argument("--copy-stages", type=int, default=0)
     p.add_argument("--copy-producers", type=int, default=0)
     p.add_argument("--copy-consumers", type=int, default=0)
+    p.add_argument("--copy-workgroups", type=int, default=0, help="staged copy: persistent grid size (0: default)")
     p.add_argument("--copy-cached", action="store_true",
                    help="staged copy: ordinary (cached) loads and stores instead of streaming ones")
     p.add_argument("--no-cpu-baseline", action="store_true")

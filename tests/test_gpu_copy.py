@@ -61,6 +61,15 @@ def test_copy_configs_multi_lap(gpu, config, stages):
     _run_copy(gpu, _bytes(7 + stages, n), stages, config)
 
 
+@pytest.mark.parametrize("workgroups", [1, 3, 100, 192, 100000])
+def test_copy_explicit_grid(gpu, workgroups):
+    # any grid size: one workgroup copying everything, grids that do not divide
+    # the tile count, and more workgroups than tiles (capped at the tile count)
+    n = 700 * 65536 + 777
+    _run_copy(gpu, _bytes(900 + workgroups, n), 2,
+              dict(copy_tile_bytes=65536, producer_waves=8, consumer_waves=8, flags=2, copy_workgroups=workgroups))
+
+
 def test_copy_special_float_bits(gpu):
     bits = np.array([0x7FC00001, 0xFFC12345, 0x80000000, 0x7F800000, 0xFF800000, 0x00000001, 0x7FBFFFFF],
                     np.uint32)
@@ -97,3 +106,6 @@ def test_copy_argument_errors(gpu):
     assert e.value.code == gpu.WSG_EUNSUPPORTED
     rc = gpu.lib.staged_copy(x.data_ptr() + 8, x.data_ptr() + 65536, 64, 2)
     assert rc == gpu.WSG_EINVAL
+    with pytest.raises(gpu.WsgError) as e:
+        gpu.staged_copy_ex(x[:1024], x[2048:3072], stages=2, config=dict(copy_workgroups=-1))
+    assert e.value.code == gpu.WSG_EINVAL

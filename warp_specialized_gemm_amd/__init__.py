@@ -57,7 +57,8 @@ class Config(ctypes.Structure):
     """struct wsg_config; zero fields mean "default"."""
     _fields_ = [("BM", ctypes.c_int), ("BN", ctypes.c_int), ("BK", ctypes.c_int),
                 ("producer_waves", ctypes.c_int), ("consumer_waves", ctypes.c_int),
-                ("copy_tile_bytes", ctypes.c_int), ("flags", ctypes.c_int), ("group_k", ctypes.c_int)]
+                ("copy_tile_bytes", ctypes.c_int), ("flags", ctypes.c_int), ("group_k", ctypes.c_int),
+                ("copy_workgroups", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -46,6 +46,7 @@ struct GemmPlan {
 
 struct CopyPlan {
     int P = 0, C = 0, tile = 0, stages = 0;
+    int workgroups = 0;  // persistent grid size requested (0: the default policy)
     const void *kernel = nullptr;
     size_t lds_bytes = 0;
 };
