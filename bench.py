@@ -20,7 +20,8 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
   copy.plain_device_copy = torch's own device-to-device copy of the same
                          buffers, the bandwidth a plain copy kernel reaches
 Options select other workloads (--workload 4: ragged fp32, --workload 5:
-bf16 8192^3) or a launch configuration (--stages, --bm/--bn/--bk,
+bf16 8192^3, --moe: a mixture-of-experts expert layer on the grouped GEMM)
+or a launch configuration (--stages, --bm/--bn/--bk,
 --producers, --consumers); --sweep prints one line per stage/producer point.
 """
 from __future__ import annotations
@@ -303,6 +304,86 @@ def run(args):
     return result
 
 
+def run_moe(args):
+    """The mixture-of-experts expert layer on the grouped GEMM: one JSON line."""
+    import numpy as np
+    import torch
+    import synth
+    import warp_specialized_gemm_amd as wsg
+    w = synth.MOE
+    rows = [int(r) for r in synth.moe_group_rows(synth.seed_for(w["id"], "A") + 50, w["tokens"], w["experts"],
+                                                    w["top_k"])]
+    G, K, N, M = w["experts"], w["K"], w["N"], sum(rows)
+    stages = args.stages or w["stages"]
+    log("generating the expert layer: %d experts, rows %s, K %d, N %d" % (G, rows, K, N))
+    A = synth.normal_bf16_bits(synth.seed_for(w["id"], "A"), M * K).reshape(M, K)
+    B = synth.normal_bf16_bits(synth.seed_for(w["id"], "B"), G * K * N).reshape(G, K, N)
+    bias = synth.normal_bf16_bits(synth.seed_for(w["id"], "bias"), G * N).reshape(G, N)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()  # noqa: E731
+    dA, dB, dbias = dev(A), dev(B), dev(bias)
+    dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    config = None
+    if args.bm or args.bn or args.bk or args.producers or args.consumers or args.group_k or args.flags:
+        config = dict(BM=args.bm, BN=args.bn, BK=args.bk, producer_waves=args.producers,
+                      consumer_waves=args.consumers, group_k=args.group_k, flags=args.flags)
+    resolved = wsg.resolve_config(wsg.WSG_BF16, M, N, K, stages, config)
+    grouped = lambda: wsg.grouped_gemm_bias_relu_ex(dA, dB, dbias, rows, dC, stages=stages, config=config)  # noqa
+    for _ in range(args.warmup):
+        grouped()
+    wsg.check_device_status()
+    flops = 2.0 * M * N * K
+    g_wall, g_kern, g_min = time_region(torch, grouped, args.steps)
+    wsg.check_device_status()
+    # the same flops as one dense GEMM: every row through expert 0's weights
+    dC_d = torch.empty_like(dC)
+    dense = lambda: wsg.gemm_bias_relu_ex(dA, dB[0], dbias[0], dC_d, stages=stages, config=config)  # noqa: E731
+    dense()
+    _, d_kern, _ = time_region(torch, dense, args.steps)
+    wsg.check_device_status()
+    del dC_d
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = flops / g_kern / 1e12
+    result = {
+        "metric": "grouped GEMM+bias+ReLU TFLOP/s (% bf16 MFMA peak)",
+        "value": round(flops * args.steps / g_wall / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(g_wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w["name"], "experts": G, "tokens": w["tokens"], "top_k": w["top_k"],
+                   "group_rows": rows, "rows": M, "K": K, "N": N, "stages": stages,
+                   "tile": [resolved["BM"], resolved["BN"], resolved["BK"]],
+                   "producer_waves": resolved["producer_waves"], "consumer_waves": resolved["consumer_waves"],
+                   "group_k": resolved["group_k"], "input": "N(0,1)*0.1 rounded to bf16; seeded top-2 routing"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_ms": round(g_kern * 1e3, 4), "kernel_ms_min": round(g_min * 1e3, 4)},
+        "dense_same_flops": {"kernel_ms": round(d_kern * 1e3, 4), "kernel_tflops": round(flops / d_kern / 1e12, 3),
+                             "grouped_over_dense_time": round(g_kern / d_kern, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        starts = np.concatenate([[0], np.cumsum(rows)])
+        # 16 consecutive rows of one expert per oracle call, experts in turn
+        want = [int(starts[e] + 16 * b + i) for b in range(4) for e in range(G) for i in range(16)
+                if 16 * b + i < rows[e]]
+        threads = oracle.host_threads()
+        done, spent, outs = 0, 0.0, []
+        while done < len(want) and spent < args.cpu_budget:
+            part = want[done:done + 16]
+            t0 = time.perf_counter()
+            outs.append(oracle.grouped_gemm_bias_relu_rows(A, B, bias, rows, part, threads=threads))
+            spent += time.perf_counter() - t0
+            done += len(part)
+        ref = np.concatenate(outs, axis=0)
+        result["cpu_baseline"] = {"value": round(2.0 * done * N * K / spent / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": "%d rows spread over the %d experts (%d x %d x %d per row), %.1f s"
+                                            % (done, G, 1, N, K, spent)}
+        s = oracle.compare(dC[want[:done]].cpu().numpy(), ref)
+        result["parity"] = {"rows_checked": done, "max_abs": s["max_abs"], "rel_fro": s["rel_fro"],
+                            "pass": bool(oracle.within_tolerance(s, "bf16"))}
+    return result
+
+
 def sweep(args):
     """Ring depth S in 2, 3, 4 x 1, 2 or 4 producer waves on the 4096^3 fp32
     GEMM (256x128 tiles, 4 consumer waves; each point takes the deepest k tile
@@ -360,6 +441,8 @@ def main():
                    help="time the GEMM kernel without roles (every wave loads, barrier, computes) instead")
     p.add_argument("--no-ablation", action="store_true", help="skip the homogeneous_baseline measurement")
     p.add_argument("--sweep", action="store_true")
+    p.add_argument("--moe", action="store_true",
+                   help="the mixture-of-experts expert layer on the grouped GEMM instead of the default step")
     p.add_argument("--wait-stats", action="store_true",
                    help="after timing, count ring flag waits per role over one launch of each kernel")
     args = p.parse_args()
@@ -369,6 +452,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.moe:
+        print(json.dumps(run_moe(args)), flush=True)
         return
     print(json.dumps(run(args)), flush=True)
 

@@ -44,7 +44,7 @@ extern "C" {
 #define WSG_ELAUNCH (-3)      /* HIP runtime error while launching; see wsg_last_error() */
 #define WSG_ETIMEOUT (-4)     /* a bounded flag wait on the device gave up (reported by wsg_check_device_status) */
 
-/* dtype codes for wsg_gemm_bias_relu_ex / wsg_gemm_resolve_config */
+/* dtype codes for gemm_bias_relu_ex, grouped_gemm_bias_relu_ex and wsg_gemm_resolve_config */
 #define WSG_FP32 0
 #define WSG_BF16 1
 
@@ -96,6 +96,35 @@ int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, cons
  */
 int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                       const void *bias, float *C, int stages, const wsg_config *cfg);
+
+/* Largest number of experts one grouped launch takes. */
+#define WSG_MAX_GROUPS 64
+
+/*
+ * Grouped GEMM + bias + ReLU for the expert layer of a mixture-of-experts
+ * model, the operator [KP] section 1.1 was tuning when it met the
+ * load-barrier-compute loop. The token rows of A are sorted by expert;
+ * expert e owns the next group_rows[e] rows and applies its own weights and
+ * biases:
+ *   C[r_e + i, :] = relu(A[r_e + i, :] @ B[e] + bias[e]),  0 <= i < group_rows[e],
+ *   r_e = group_rows[0] + ... + group_rows[e - 1].
+ *   groups      1 .. WSG_MAX_GROUPS (< 1: WSG_EINVAL; above: WSG_EUNSUPPORTED).
+ *   group_rows  HOST array of `groups` row counts >= 0 (0: an expert with no
+ *               tokens); read during the call, not kept. Their sum is A's and
+ *               C's row count.
+ *   A           rows x K;  B  `groups` blocks of K x N, B[e*K*N + k*N + n];
+ *   bias        groups x N;  C  rows x N (fp32).
+ *   dtype, stages, cfg, alignment and overlap rules as gemm_bias_relu_ex, with
+ *   B and bias at their full sizes. The default tile is chosen for the total
+ *   row count.
+ * One launch covers every expert's tiles (each expert's rows are tiled on
+ * their own, so its last tile row is ragged); every expert's rows equal what
+ * gemm_bias_relu_ex returns for that expert's slice with the same explicit
+ * configuration.
+ */
+int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, int64_t N, int64_t K,
+                              const void *A, const void *B, const void *bias, float *C, int stages,
+                              const wsg_config *cfg);
 
 /*
  * WSG_FLAG_HOMOGENEOUS selects the kernel the wave-specialized one is measured

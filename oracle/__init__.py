@@ -14,6 +14,8 @@ Contents
     the double-buffered load/store example of "Producer-Consumer Warp
     Specialization for TMA Operations".
   * ringsim: a simulator of the full/empty ring protocol (oracle/ringsim.py).
+  * grouped_gemm_bias_relu / grouped_gemm_bias_relu_rows: the same operator
+    once per expert of a mixture-of-experts layer (oracle/grouped.py).
 """
 from __future__ import annotations
 
@@ -170,6 +172,18 @@ def gemm_bias_relu_rows(A, B, bias, rows, threads: int | None = None) -> np.ndar
 
 def gemm_bias_relu_at(A, B, bias, ms, ns, threads: int | None = None) -> np.ndarray:
     return default().gemm_bias_relu_at(A, B, bias, ms, ns, threads)
+
+
+def grouped_gemm_bias_relu(A, B, bias, group_rows, threads: int | None = None) -> np.ndarray:
+    from . import grouped
+    return grouped.grouped_gemm_bias_relu(A, B, bias, group_rows,
+                                          lambda a, b, c: gemm_bias_relu(a, b, c, threads))
+
+
+def grouped_gemm_bias_relu_rows(A, B, bias, group_rows, rows, threads: int | None = None) -> np.ndarray:
+    from . import grouped
+    return grouped.grouped_gemm_bias_relu_rows(A, B, bias, group_rows, rows,
+                                               lambda a, b, c, r: gemm_bias_relu_rows(a, b, c, r, threads))
 
 
 def copy(src: np.ndarray, threads: int | None = None) -> np.ndarray:

@@ -13,7 +13,11 @@ synthetic):
   * bf16 operands: N(0, 1) * 0.1 by Box-Muller in fp64, rounded to fp32 and
     then to bf16, both round-to-nearest-even;
   * integer-valued operands for bit-exact parity: uniform on {lo..hi};
-  * per-tensor seed = 1000 * workload_id + {A: 1, B: 2, bias: 3, src: 4}.
+  * per-tensor seed = 1000 * workload_id + {A: 1, B: 2, bias: 3, src: 4};
+  * mixture-of-experts routing (row counts per expert): each token takes its
+    top_k experts by score = uniform noise + 0.3 * a per-expert popularity
+    offset (both uniform on [-1, 1)), so experts get uneven loads, as with a
+    learned router; see moe_group_rows.
 """
 from __future__ import annotations
 
@@ -26,7 +30,7 @@ __all__ = [
     "GOLDEN", "MUL1", "MUL2", "WORKLOADS", "TENSOR_IDS",
     "seed_for", "splitmix64", "uniform_pm1", "normal_bf16_bits",
     "small_int_f32", "small_int_bf16_bits", "f32_to_bf16_bits_rne",
-    "bf16_bits_to_f32",
+    "bf16_bits_to_f32", "MOE", "moe_group_rows",
 ]
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -75,6 +79,27 @@ WORKLOADS = {
             stages=4,
             name="bf16 gemm+bias+relu 8192x8192x8192, fp32 accumulate and output"),
 }
+
+
+# The expert layer of a mixture-of-experts model for the grouped GEMM: 8
+# experts, 4096 tokens routed to their top 2, model width K = 4096, expert
+# width N = 14336 (the shape of a widely used open 8-expert model; the pages
+# name none), bf16 operands as workload 5. Seeds use workload id 6.
+MOE = dict(kind="grouped_gemm", dtype="bf16", experts=8, tokens=4096, top_k=2, K=4096, N=14336,
+           dist="normal0.1", stages=4, id=6,
+           name="bf16 grouped gemm+bias+relu, 8 experts, 4096 tokens top-2, K 4096, N 14336")
+
+
+def moe_group_rows(seed: int, tokens: int, experts: int, top_k: int) -> np.ndarray:
+    """Rows per expert (int64, length `experts`, summing to tokens * top_k):
+    every token picks the top_k experts by its seeded score."""
+    if not 1 <= top_k <= experts:
+        raise ValueError("top_k must be in 1..experts")
+    popularity = uniform_pm1(seed, experts).astype(np.float64)
+    noise = uniform_pm1(seed + 1, tokens * experts).astype(np.float64).reshape(tokens, experts)
+    score = noise + 0.3 * popularity
+    top = np.argsort(-score, axis=1, kind="stable")[:, :top_k]
+    return np.bincount(top.ravel(), minlength=experts).astype(np.int64)
 
 
 def seed_for(workload_id: int, tensor: str) -> int:

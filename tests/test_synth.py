@@ -51,3 +51,13 @@ def test_small_ints_cover_range():
 def test_seeds_distinct_per_tensor():
     seeds = {synth.seed_for(w, t) for w in synth.WORKLOADS for t in synth.TENSOR_IDS}
     assert len(seeds) == len(synth.WORKLOADS) * len(synth.TENSOR_IDS)
+
+
+def test_moe_group_rows():
+    rows = synth.moe_group_rows(600, 4096, 8, 2)
+    assert rows.dtype == np.int64 and rows.shape == (8,)
+    assert rows.sum() == 4096 * 2 and rows.max() <= 4096 and rows.min() >= 0
+    assert rows.max() > 1.5 * rows.min()  # uneven loads
+    assert np.array_equal(rows, synth.moe_group_rows(600, 4096, 8, 2))
+    assert not np.array_equal(rows, synth.moe_group_rows(601, 4096, 8, 2))
+    assert synth.moe_group_rows(1, 10, 4, 4).tolist() == [10, 10, 10, 10]

@@ -8,7 +8,7 @@ exceptions. There is no fallback: if libwsg.so is missing or fails to load,
 importing this package raises.
 
 Names follow the C ABI: gemm_bias_relu, gemm_bias_relu_bf16,
-gemm_bias_relu_ex, staged_copy, staged_copy_ex, resolve_config,
+gemm_bias_relu_ex, grouped_gemm_bias_relu_ex, staged_copy, staged_copy_ex, resolve_config,
 check_device_status, set_stream, get_stream, last_error, version.
 """
 from __future__ import annotations
@@ -18,11 +18,11 @@ import os
 
 __all__ = [
     "WsgError", "Config", "lib", "library_path", "EXPORTS",
-    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "resolve_config",
+    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "resolve_config",
     "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
     "set_stream", "get_stream",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
-    "WSG_FLAG_HOMOGENEOUS",
+    "WSG_FLAG_HOMOGENEOUS", "WSG_MAX_GROUPS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,11 +38,12 @@ WSG_BF16 = 1
 WSG_FLAG_GENERAL_PRODUCER = 1
 WSG_FLAG_NONTEMPORAL = 2
 WSG_FLAG_HOMOGENEOUS = 4
+WSG_MAX_GROUPS = 64
 
 # every function include/wsg.h declares
 EXPORTS = (
-    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "wsg_gemm_resolve_config",
-    "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
+    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex",
+    "wsg_gemm_resolve_config", "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
     "wsg_check_device_status", "wsg_set_wait_stats", "wsg_read_wait_stats", "wsg_version",
 )
 
@@ -79,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "gemm_bias_relu": ([i64, i64, i64, vp, vp, vp, vp, ci], ci),
         "gemm_bias_relu_bf16": ([i64, i64, i64, vp, vp, vp, vp, ci], ci),
         "gemm_bias_relu_ex": ([ci, i64, i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
+        "grouped_gemm_bias_relu_ex": ([ci, ci, ctypes.POINTER(i64), i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
         "wsg_gemm_resolve_config": ([ci, i64, i64, i64, ci, cfgp, cfgp], ci),
         "staged_copy": ([vp, vp, ctypes.c_size_t, ci], ci),
         "staged_copy_ex": ([vp, vp, ctypes.c_size_t, ci, cfgp], ci),
@@ -196,6 +198,44 @@ def gemm_bias_relu_ex(A, B, bias, C=None, stages: int = 4, config=None):
     _use_current_stream()
     _raise_on(lib.gemm_bias_relu_ex(dtype, M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr(), C.data_ptr(),
                                     stages, _config(config)))
+    return C
+
+
+def grouped_gemm_bias_relu_ex(A, B, bias, group_rows, C=None, stages: int = 4, config=None):
+    """Mixture-of-experts GEMM: A's rows sorted by expert, group_rows[e] of them
+    for expert e; B is (experts, K, N), bias (experts, N). Returns C (rows, N)
+    with C[rows of e] = relu(A[rows of e] @ B[e] + bias[e])."""
+    import torch
+    if not isinstance(A, torch.Tensor):
+        raise TypeError("A must be a CUDA (HIP) tensor")
+    if A.dtype == torch.float32:
+        dtype, ok = WSG_FP32, (torch.float32,)
+    else:
+        dtype, ok = WSG_BF16, _bf16_ok()
+    for name, t in (("A", A), ("B", B), ("bias", bias)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+        if t.dtype not in ok:
+            raise TypeError("%s must have dtype in %s, got %s" % (name, ok, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous (row-major)" % name)
+    rows = [int(r) for r in group_rows]
+    G = len(rows)
+    if A.dim() != 2 or B.dim() != 3 or bias.dim() != 2:
+        raise ValueError("A must be rows x K, B experts x K x N and bias experts x N")
+    M, K = A.shape
+    if tuple(B.shape[:2]) != (G, K) or tuple(bias.shape) != (G, B.shape[2]) or sum(rows) != M:
+        raise ValueError("shape mismatch: A %s, B %s, bias %s, %d experts with %d rows" % (
+            tuple(A.shape), tuple(B.shape), tuple(bias.shape), G, sum(rows)))
+    N = B.shape[2]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif C.dtype != torch.float32 or tuple(C.shape) != (M, N) or not C.is_contiguous() or not C.is_cuda:
+        raise ValueError("C must be a contiguous float32 CUDA tensor of shape (%d, %d)" % (M, N))
+    counts = (ctypes.c_int64 * max(G, 1))(*rows)
+    _use_current_stream()
+    _raise_on(lib.grouped_gemm_bias_relu_ex(dtype, G, counts, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr(),
+                                            C.data_ptr(), stages, _config(config)))
     return C
 
 

@@ -80,14 +80,15 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
 constexpr uint64_t kMaxElems = 1ull << 56;  // per operand: keeps every byte count well inside size_t
 
+// `blocks` B and bias blocks (the experts of a grouped launch; 1 otherwise)
 int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
-                  const float *C, int stages) {
+                  const float *C, int stages, int64_t blocks = 1) {
     if (dtype != WSG_FP32 && dtype != WSG_BF16) return fail(WSG_EINVAL, "dtype must be WSG_FP32 or WSG_BF16");
     if (M < 0 || N < 0 || K < 0) return fail(WSG_EINVAL, "negative dimension");
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(WSG_EUNSUPPORTED, "dimension above 2^31 - 1");
     if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
     if (M == 0 || N == 0) return WSG_OK;
-    if ((uint64_t)M * (uint64_t)K > kMaxElems || (uint64_t)K * (uint64_t)N > kMaxElems ||
+    if ((uint64_t)M * (uint64_t)K > kMaxElems || (uint64_t)K * (uint64_t)N > kMaxElems / (uint64_t)blocks ||
         (uint64_t)M * (uint64_t)N > kMaxElems)
         return fail(WSG_EUNSUPPORTED, "operand larger than 2^56 elements");
     const size_t esz = dtype == WSG_FP32 ? 4 : 2;
@@ -97,8 +98,9 @@ int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, con
         return fail(WSG_EINVAL, "A, B and bias must be aligned to their element size");
     if ((uintptr_t)C % 4) return fail(WSG_EINVAL, "C must be 4-byte aligned");
     const size_t cbytes = (size_t)M * (size_t)N * 4;
-    if (overlaps(C, cbytes, A, (size_t)M * (size_t)K * esz) || overlaps(C, cbytes, B, (size_t)K * (size_t)N * esz) ||
-        overlaps(C, cbytes, bias, (size_t)N * esz))
+    if (overlaps(C, cbytes, A, (size_t)M * (size_t)K * esz) ||
+        overlaps(C, cbytes, B, (size_t)blocks * (size_t)K * (size_t)N * esz) ||
+        overlaps(C, cbytes, bias, (size_t)blocks * (size_t)N * esz))
         return fail(WSG_EINVAL, "C overlaps an input");
     return WSG_OK;
 }
@@ -118,6 +120,34 @@ int gemm_impl(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     rc = wsg::plan_gemm(dtype, M, N, K, A, B, stages, cfg, ctx.dev, &plan, &err);
     if (rc != WSG_OK) return fail(rc, err);
     rc = wsg::launch_gemm(ctx, plan, M, N, K, A, B, bias, C, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    return ok();
+}
+
+int grouped_impl(int dtype, int groups, const int64_t *group_rows, int64_t N, int64_t K, const void *A, const void *B,
+                 const void *bias, float *C, int stages, const wsg_config *cfg) {
+    if (groups < 1) return fail(WSG_EINVAL, "groups must be >= 1");
+    if (groups > WSG_MAX_GROUPS) return fail(WSG_EUNSUPPORTED, "more than WSG_MAX_GROUPS experts");
+    if (!group_rows) return fail(WSG_EINVAL, "null group_rows");
+    int64_t rows = 0;
+    for (int e = 0; e < groups; ++e) {
+        if (group_rows[e] < 0) return fail(WSG_EINVAL, "negative row count for an expert");
+        if (group_rows[e] > kMaxDim - rows) return fail(WSG_EUNSUPPORTED, "total rows above 2^31 - 1");
+        rows += group_rows[e];
+    }
+    int rc = validate_gemm(dtype, rows, N, K, A, B, bias, C, stages, groups);
+    if (rc != WSG_OK) return rc;
+    if (rows == 0 || N == 0) return ok();
+    wsg::LaunchCtx ctx;
+    rc = device_info(&ctx.dev);
+    if (rc != WSG_OK) return rc;
+    ctx.stream = tl_stream;
+    ctx.wait_stats = tl_wait_stats;
+    wsg::GemmPlan plan;
+    std::string err;
+    rc = wsg::plan_gemm(dtype, rows, N, K, A, B, stages, cfg, ctx.dev, &plan, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    rc = wsg::launch_grouped_gemm(ctx, plan, groups, group_rows, N, K, A, B, bias, C, &err);
     if (rc != WSG_OK) return fail(rc, err);
     return ok();
 }
@@ -188,6 +218,11 @@ int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, cons
 int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                       float *C, int stages, const wsg_config *cfg) {
     return gemm_impl(dtype, M, N, K, A, B, bias, C, stages, cfg);
+}
+
+int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, int64_t N, int64_t K, const void *A,
+                              const void *B, const void *bias, float *C, int stages, const wsg_config *cfg) {
+    return grouped_impl(dtype, groups, group_rows, N, K, A, B, bias, C, stages, cfg);
 }
 
 int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stages, const wsg_config *cfg,

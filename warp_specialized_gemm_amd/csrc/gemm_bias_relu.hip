@@ -77,12 +77,14 @@ constexpr int kXcds = 8;
 
 // kGroupRows tile rows per group: 8 for square tiles; for tall tiles fewer
 // rows (and so more columns) keep the A and B bytes a group touches balanced.
-template <int kGroupRows>
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
-    const int G = tiles_m * tiles_n;
+__device__ __forceinline__ int xcd_linear(int bid, int total) {
     const int x = bid % kXcds, i = bid / kXcds;
-    const int q = G / kXcds, r = G % kXcds;
-    const int L = x * q + min(x, r) + i;
+    const int q = total / kXcds, r = total % kXcds;
+    return x * q + min(x, r) + i;
+}
+
+template <int kGroupRows>
+__device__ __forceinline__ void swizzle_tile(int L, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int per_group = kGroupRows * tiles_n;
     const int grp = L / per_group;
     const int first_m = grp * kGroupRows;
@@ -90,6 +92,82 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     const int rem = L - grp * per_group;
     tm = first_m + rem % gm;
     tn = rem / gm;
+}
+
+// Grouped launches: the experts of a mixture-of-experts layer, each applying
+// its own weights and biases to the token rows routed to it (rows sorted by
+// expert). Expert e owns rows row0[e] .. row0[e + 1] - 1 of A and C, the e-th
+// K x N block of B, the e-th N biases, and the launch's logical tiles
+// tile0[e] .. tile0[e + 1] - 1 (empty experts own none); entries past the
+// last expert repeat the totals. The table travels in the kernel arguments.
+struct GroupTable {
+    int n;
+    int tile0[WSG_MAX_GROUPS + 1];
+    int64_t row0[WSG_MAX_GROUPS + 1];
+};
+
+// Kernel arguments of a grouped launch: the GEMM's (with the whole launch's
+// pointers) plus the expert table. Ordinary launches pass GemmArgs alone, so
+// their kernels are compiled exactly as without grouping.
+struct GroupedArgs {
+    GemmArgs a;
+    GroupTable gt;
+};
+template <bool GR>
+struct KernelArgs {
+    using type = GemmArgs;
+};
+template <>
+struct KernelArgs<true> {
+    using type = GroupedArgs;
+};
+__device__ __forceinline__ GemmArgs &gemm_args(GemmArgs &p) { return p; }
+__device__ __forceinline__ GemmArgs &gemm_args(GroupedArgs &p) { return p.a; }
+
+template <int kGroupRows>
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
+    swizzle_tile<kGroupRows>(xcd_linear(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+}
+
+// Workgroup -> (tile row, tile column). For a grouped launch it also points
+// the GEMM arguments at the expert's operands and row count; the XCD step
+// runs over the whole launch, so each XCD's run of tiles stays contiguous
+// across experts.
+template <int kGroupRows, int BM, int ES>
+__device__ __forceinline__ void resolve_tile(GemmArgs &a, int &tm, int &tn) {
+    tile_coords<kGroupRows>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+}
+template <int kGroupRows, int BM, int ES>
+__device__ __forceinline__ void resolve_tile(GroupedArgs &p, int &tm, int &tn) {
+    GemmArgs &a = p.a;
+    const GroupTable &gt = p.gt;
+    const int L = xcd_linear(blockIdx.x, gt.tile0[WSG_MAX_GROUPS]);
+    // tile0 is nondecreasing (entries past the last expert hold the totals):
+    // the expert is the last entry at or below L, its end the first above.
+    // Constant indices only, so the table is read with scalar loads rather
+    // than copied to scratch memory for a dynamic index.
+    int e = 0, t0 = 0;
+    int64_t r0 = 0, r1 = 0;
+    bool above = false;
+#pragma unroll
+    for (int i = 1; i <= WSG_MAX_GROUPS; ++i) {
+        const int ti = gt.tile0[i];
+        if (ti <= L) {
+            e = i;
+            t0 = ti;
+            r0 = gt.row0[i];
+        } else if (!above) {
+            r1 = gt.row0[i];
+            above = true;
+        }
+    }
+    a.M = r1 - r0;
+    a.tiles_m = (int)((a.M + BM - 1) / BM);
+    a.A += (size_t)r0 * (size_t)a.K * ES;
+    a.B += (size_t)e * (size_t)a.K * (size_t)a.N * ES;
+    a.bias += (size_t)e * (size_t)a.N * ES;  // the bias has the operands' element type
+    a.C += r0 * a.N;
+    swizzle_tile<kGroupRows>(L - t0, a.tiles_m, a.tiles_n, tm, tn);
 }
 
 // Kernel prologue for the ring's flags: zero the LDS flag words, then the
@@ -462,8 +540,9 @@ __device__ __forceinline__ void sync_loop(const GemmArgs &a, unsigned char *ring
 // ----------------------------------------------------------------------------
 // fp32 kernel
 // ----------------------------------------------------------------------------
-template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA>
-__global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs a) {
+template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA, bool GR>
+__global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename KernelArgs<GR>::type ka) {
+    GemmArgs &a = gemm_args(ka);
     constexpr int NCW = CWM * CWN;
     constexpr int WTM = BM / CWM, WTN = BN / CWN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -480,7 +559,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
     const LdsFlags fl = init_flags(lds);
 
     int tm, tn;
-    tile_coords<(8 * BN / BM > 0 ? 8 * BN / BM : 1)>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    resolve_tile<(8 * BN / BM > 0 ? 8 * BN / BM : 1), BM, 4>(ka, tm, tn);
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int T = (int)((K + BK - 1) / BK);
@@ -594,8 +673,9 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(GemmArgs
 // ----------------------------------------------------------------------------
 // GK: k per fragment group (16 or 32). A deeper group gives each consumer
 // step more MFMA work to hide the next group's LDS reads behind.
-template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA, int GK>
-__global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArgs a) {
+template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA, int GK, bool GR>
+__global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typename KernelArgs<GR>::type ka) {
+    GemmArgs &a = gemm_args(ka);
     constexpr int NCW = CWM * CWN;
     constexpr int WTM = BM / CWM, WTN = BN / CWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -613,7 +693,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(GemmArg
     const LdsFlags fl = init_flags(lds);
 
     int tm, tn;
-    tile_coords<(8 * BN / BM > 0 ? 8 * BN / BM : 1)>(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    resolve_tile<(8 * BN / BM > 0 ? 8 * BN / BM : 1), BM, 2>(ka, tm, tn);
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int T = (int)((K + BK - 1) / BK);
@@ -743,10 +823,12 @@ namespace {
 
 #define WSG_F32(BM, BN, BK, P, CWM, CWN, DMA)                                                              \
     {WSG_FP32, BM, BN, BK, P, CWM, CWN, DMA, 16,                                                           \
-     reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA>)}
+     reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA, false>),                \
+     reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA, true>)}
 #define WSG_BF(BM, BN, BK, P, CWM, CWN, DMA, GK)                                                           \
     {WSG_BF16, BM, BN, BK, P, CWM, CWN, DMA, GK,                                                           \
-     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK>)}
+     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK, false>),           \
+     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK, true>)}
 
 // When the caller leaves fields at 0, the first variant (in this order) whose
 // tile matches the size class and whose ring fits in LDS wins.
@@ -886,9 +968,30 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     return WSG_OK;
 }
 
-int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N, int64_t K, const void *A,
-                const void *B, const void *bias, float *C, std::string *err) {
-    if (M == 0 || N == 0) return WSG_OK;
+namespace {
+
+void fill_common(const LaunchCtx &ctx, const GemmPlan &plan, GemmArgs &args) {
+    args.S = plan.stages;
+    args.tiles_n = (int)plan.tiles_n;
+    args.status = ctx.dev.status;
+    args.stats = ctx.wait_stats ? ctx.dev.stats : nullptr;
+}
+
+int launch_with(const LaunchCtx &ctx, const GemmPlan &plan, const void *kernel, void *kernel_args, int64_t grid,
+                std::string *err) {
+    const int threads = (plan.v->P + plan.v->CWM * plan.v->CWN) * 64;
+    const int rc = prepare_kernel(kernel, ctx.dev, err);
+    if (rc != WSG_OK) return rc;
+    void *kargs[] = {kernel_args};
+    hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(threads), kargs, plan.lds_bytes, ctx.stream);
+    if (e != hipSuccess) {
+        *err = std::string("gemm launch: ") + hipGetErrorString(e);
+        return WSG_ELAUNCH;
+    }
+    return WSG_OK;
+}
+
+GemmArgs make_args(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, float *C) {
     GemmArgs args;
     args.A = static_cast<const unsigned char *>(A);
     args.B = static_cast<const unsigned char *>(B);
@@ -897,22 +1000,51 @@ int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N
     args.M = M;
     args.N = N;
     args.K = K;
-    args.S = plan.stages;
+    return args;
+}
+
+}  // namespace
+
+int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N, int64_t K, const void *A,
+                const void *B, const void *bias, float *C, std::string *err) {
+    if (M == 0 || N == 0) return WSG_OK;
+    GemmArgs args = make_args(M, N, K, A, B, bias, C);
+    fill_common(ctx, plan, args);
     args.tiles_m = (int)plan.tiles_m;
-    args.tiles_n = (int)plan.tiles_n;
-    args.status = ctx.dev.status;
-    args.stats = ctx.wait_stats ? ctx.dev.stats : nullptr;
-    const int threads = (plan.v->P + plan.v->CWM * plan.v->CWN) * 64;
-    const int rc = prepare_kernel(plan.v->kernel, ctx.dev, err);
-    if (rc != WSG_OK) return rc;
-    void *kargs[] = {&args};
-    hipError_t e = hipLaunchKernel(plan.v->kernel, dim3((unsigned)(plan.tiles_m * plan.tiles_n)), dim3(threads), kargs,
-                        plan.lds_bytes, ctx.stream);
-    if (e != hipSuccess) {
-        *err = std::string("gemm launch: ") + hipGetErrorString(e);
-        return WSG_ELAUNCH;
+    return launch_with(ctx, plan, plan.v->kernel, &args, plan.tiles_m * plan.tiles_n, err);
+}
+
+int launch_grouped_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int groups, const int64_t *group_rows, int64_t N,
+                        int64_t K, const void *A, const void *B, const void *bias, float *C, std::string *err) {
+    if (groups < 1 || groups > WSG_MAX_GROUPS) {
+        *err = "groups must be in 1.." + std::to_string(WSG_MAX_GROUPS);
+        return WSG_EUNSUPPORTED;
     }
-    return WSG_OK;
+    if (N == 0) return WSG_OK;
+    GroupedArgs ga;
+    GroupTable &gt = ga.gt;
+    gt.n = groups;
+    gt.row0[0] = 0;
+    gt.tile0[0] = 0;
+    int64_t tiles = 0;
+    for (int e = 0; e < groups; ++e) {
+        gt.row0[e + 1] = gt.row0[e] + group_rows[e];
+        tiles += (group_rows[e] + plan.v->BM - 1) / plan.v->BM * plan.tiles_n;
+        if (tiles > 0x7FFFFFFF) {
+            *err = "too many output tiles";
+            return WSG_EUNSUPPORTED;
+        }
+        gt.tile0[e + 1] = (int)tiles;
+    }
+    for (int e = groups + 1; e <= WSG_MAX_GROUPS; ++e) {
+        gt.row0[e] = gt.row0[groups];
+        gt.tile0[e] = gt.tile0[groups];
+    }
+    if (tiles == 0) return WSG_OK;
+    ga.a = make_args(gt.row0[groups], N, K, A, B, bias, C);
+    fill_common(ctx, plan, ga.a);
+    ga.a.tiles_m = 0;  // per expert, set on the device
+    return launch_with(ctx, plan, plan.v->grouped_kernel, &ga, tiles, err);
 }
 
 }  // namespace wsg

@@ -34,7 +34,8 @@ struct GemmVariant {
     int CWM, CWN; // consumer wave grid
     bool dma;     // LDS-DMA producer (aligned shapes) or register-staged producer (any shape)
     int GK;       // consumer k per fragment group
-    const void *kernel;
+    const void *kernel;          // ordinary launch
+    const void *grouped_kernel;  // the same kernel for a grouped (mixture-of-experts) launch
 };
 
 struct GemmPlan {
@@ -64,6 +65,11 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
               const wsg_config *cfg, const DeviceInfo &dev, GemmPlan *plan, std::string *err);
 int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N, int64_t K, const void *A,
                 const void *B, const void *bias, float *C, std::string *err);
+// One launch over the tiles of `groups` experts (rows sorted by expert,
+// group_rows[e] rows each; B and bias hold one block per expert); `plan` was
+// made for the total row count.
+int launch_grouped_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int groups, const int64_t *group_rows, int64_t N,
+                        int64_t K, const void *A, const void *B, const void *bias, float *C, std::string *err);
 
 int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo &dev, CopyPlan *plan,
               std::string *err);
