@@ -354,7 +354,9 @@ def run_moe(args):
                    "producer_waves": resolved["producer_waves"], "consumer_waves": resolved["consumer_waves"],
                    "group_k": resolved["group_k"], "input": "N(0,1)*0.1 rounded to bf16; seeded top-2 routing"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic("grouped_moe_%s" % "x".join(str(resolved[k]) for k in
+                                                                              ("BM", "BN", "BK")), "gemm"),
                      "kernel_ms": round(g_kern * 1e3, 4), "kernel_ms_min": round(g_min * 1e3, 4)},
         "dense_same_flops": {"kernel_ms": round(d_kern * 1e3, 4), "kernel_tflops": round(flops / d_kern / 1e12, 3),
                              "grouped_over_dense_time": round(g_kern / d_kern, 4)},
