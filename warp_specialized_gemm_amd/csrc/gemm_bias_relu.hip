@@ -420,7 +420,12 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 // that early value shows the tile unpublished does the wave spin on it.
 // Returns false if a wait gave up.
 // ----------------------------------------------------------------------------
-template <int KG, int P, typename Frag, typename Flags, typename Read, typename Mma>
+// IL > 0: the next group's fragment reads and the current group's MFMAs form
+// one straight-line block (on the last step the reads repeat the current
+// group, harmlessly), and the scheduler is asked to alternate them, IL pairs
+// of one MFMA and one LDS read, so the reads issue in the shadow of the MFMAs
+// instead of in a burst between them.
+template <int KG, int P, typename Frag, int IL = 0, typename Flags, typename Read, typename Mma>
 __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, int slot_bytes, const Flags &fl,
                                              unsigned *status, WaitTally &tally, Read read, Mma mma) {
     const int U = T * KG;
@@ -441,8 +446,30 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
             fl.arrive_empty(cs);
             if (++cs == S) cs = 0;
         }
-        if (u + 1 < U) {
-            if (++rg == KG) {
+        if constexpr (IL == 0) {
+            if (u + 1 < U) {
+                if (++rg == KG) {
+                    rg = 0;
+                    if (++rs == S) {
+                        rs = 0;
+                        ++rlap;
+                    }
+                    if (phase_of<P>(pk) == (rlap & 1u)) {
+                        if (!fl.template wait_full<P>(rs, rlap & 1u, status, kStatusGemm, tally)) {
+                            alive = false;
+                            return;
+                        }
+                    } else {
+                        ++tally.waits;  // satisfied by the early read
+                    }
+                    asm volatile("" ::: "memory");
+                }
+                read(nxt, ring + (size_t)rs * slot_bytes, rg);
+                if (rg == KG - 1 && u + 1 + KG < U) peek = fl.peek_full(rs + 1 == S ? 0 : rs + 1);
+            }
+            mma(cur);
+        } else {
+            if (u + 1 < U && ++rg == KG) {
                 rg = 0;
                 if (++rs == S) {
                     rs = 0;
@@ -458,10 +485,16 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
                 }
                 asm volatile("" ::: "memory");
             }
+            const uint32_t pv = fl.peek_full(rs + 1 == S ? 0 : rs + 1);
             read(nxt, ring + (size_t)rs * slot_bytes, rg);
-            if (rg == KG - 1 && u + 1 + KG < U) peek = fl.peek_full(rs + 1 == S ? 0 : rs + 1);
+            mma(cur);
+            peek = (rg == KG - 1 && u + 1 + KG < U) ? pv : peek;
+#pragma unroll
+            for (int i = 0; i < IL; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
         }
-        mma(cur);
     };
     for (int u = 0; alive && u < U; u += 2) {
         step(u, f0, f1);
@@ -779,7 +812,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
         sync_loop<BM, BN, BK, 2, NCW, KG, Frag>(a, ring, cw, lane, m0, n0, T, read, mma);
     } else {
         WaitTally tally;
-        if (!consume_ring<KG, P, Frag>(T, S, ring, SLOT, fl, a.status, tally, read, mma)) return;
+        if (!consume_ring<KG, P, Frag, GS * FM * FN>(T, S, ring, SLOT, fl, a.status, tally, read, mma)) return;
         publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
     }
 
@@ -853,12 +886,13 @@ const GemmVariant kGemmVariants[] = {
     WSG_F32(256, 128, 32, 0, 4, 2, true),  WSG_F32(256, 128, 16, 0, 4, 2, true),
     WSG_F32(128, 128, 32, 0, 2, 2, true),
     WSG_F32(64, 64, 16, 0, 2, 2, true),
-    // bf16, wave-specialized
+    // bf16, wave-specialized. Two producer waves first: with one, consumers
+    // found the next tile unpublished at 41% of their waits (8192^3, S = 4).
     WSG_BF(256, 128, 64, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 2, 2, 2, true, 16),
-    WSG_BF(256, 128, 64, 1, 2, 2, true, 32),  WSG_BF(256, 128, 32, 1, 2, 2, true, 32),
-    WSG_BF(256, 128, 32, 1, 2, 2, true, 16),
+    WSG_BF(256, 128, 32, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 1, 2, 2, true, 32),
+    WSG_BF(256, 128, 32, 1, 2, 2, true, 32),  WSG_BF(256, 128, 32, 1, 2, 2, true, 16),
     WSG_BF(256, 128, 64, 4, 2, 2, true, 32),  WSG_BF(256, 128, 32, 4, 2, 2, true, 32),
-    WSG_BF(256, 128, 32, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 4, 2, 2, true, 16),
+    WSG_BF(256, 128, 64, 4, 2, 2, true, 16),
     WSG_BF(256, 128, 32, 4, 2, 2, true, 16),  WSG_BF(256, 128, 32, 2, 2, 2, true, 16),
     WSG_BF(128, 128, 64, 1, 2, 2, true, 32),  WSG_BF(128, 128, 32, 1, 2, 2, true, 16),
     WSG_BF(64, 64, 32, 1, 2, 2, true, 16),    WSG_BF(256, 128, 32, 1, 2, 2, false, 32),
