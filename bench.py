@@ -20,7 +20,8 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
   copy.plain_device_copy = torch's own device-to-device copy of the same
                          buffers, the bandwidth a plain copy kernel reaches
 Options select other workloads (--workload 4: ragged fp32, --workload 5:
-bf16 8192^3, --moe: a mixture-of-experts expert layer on the grouped GEMM)
+bf16 8192^3, --moe: a mixture-of-experts expert layer on the grouped GEMM,
+--attention: attention forward)
 or a launch configuration (--stages, --bm/--bn/--bk,
 --producers, --consumers); --sweep prints one line per stage/producer point.
 """
@@ -386,6 +387,82 @@ def run_moe(args):
     return result
 
 
+def run_attention_bench(args):
+    """Attention forward (the second consumer type): one JSON line, non-causal headline plus the causal run."""
+    import math
+    import numpy as np
+    import torch
+    import synth
+    import warp_specialized_gemm_amd as wsg
+    w = synth.ATTENTION
+    Bn, H, S, D = w["batch"], w["heads"], w["S"], w["D"]
+    stages = args.stages or w["stages"]
+    n = Bn * H * S * D
+    log("generating attention inputs %s" % ((Bn, H, S, D),))
+    Q = synth.normal_bf16_bits(synth.seed_for(w["id"], "A"), n, scale=1.0).reshape(Bn, H, S, D)
+    K = synth.normal_bf16_bits(synth.seed_for(w["id"], "B"), n, scale=1.0).reshape(Bn, H, S, D)
+    V = synth.normal_bf16_bits(synth.seed_for(w["id"], "src"), n, scale=1.0).reshape(Bn, H, S, D)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()  # noqa: E731
+    dQ, dK, dV = dev(Q), dev(K), dev(V)
+    dO = torch.empty((Bn, H, S, D), dtype=torch.float32, device="cuda")
+    config = dict(producer_waves=args.producers) if args.producers else None
+    peak = PEAK_TFLOPS["bf16"]
+    out = {}
+    for causal in (False, True):
+        fn = lambda: wsg.attention_fwd(dQ, dK, dV, dO, causal=causal, stages=stages, config=config)  # noqa: E731
+        for _ in range(args.warmup):
+            fn()
+        wsg.check_device_status()
+        wall, kern, kmin = time_region(torch, fn, args.steps)
+        wsg.check_device_status()
+        pairs = S * (S + 1) // 2 if causal else S * S  # (query, key) pairs that count
+        flops = 4.0 * Bn * H * pairs * D
+        out[causal] = (flops, wall, kern, kmin)
+    flops, wall, kern, kmin = out[False]
+    result = {
+        "metric": "attention forward TFLOP/s (% bf16 MFMA peak)",
+        "value": round(flops * args.steps / wall / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w["name"], "batch": Bn, "heads": H, "Sq": S, "Skv": S, "D": D, "stages": stages,
+                   "producer_waves": args.producers or 2, "consumer_waves": 4, "queries_per_workgroup": 128,
+                   "keys_per_slot": 64, "input": "N(0,1) rounded to bf16, scale 1/sqrt(D)"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / kern / 1e12, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / kern / 1e12 / peak, 4), "traffic": None,
+                     "kernel_ms": round(kern * 1e3, 4), "kernel_ms_min": round(kmin * 1e3, 4)},
+    }
+    cf, cw, ck, cm = out[True]
+    result["causal"] = {"value": round(cf * args.steps / cw / 1e12, 3), "unit": "TFLOP/s",
+                        "kernel_tflops": round(cf / ck / 1e12, 3), "frac": round(cf / ck / 1e12 / peak, 4),
+                        "kernel_ms": round(ck * 1e3, 4), "flops": cf}
+    if not args.no_cpu_baseline:
+        import oracle
+        import oracle.attention as att
+        from threadpoolctl import threadpool_limits
+        threads = oracle.host_threads()
+        # the causal output is still in dO: rows of head (0, 0), 32 at a time, against the oracle
+        got = dO[0, 0].cpu().numpy()
+        done, spent, refs, rows_all = 0, 0.0, [], []
+        with threadpool_limits(limits=threads):
+            while done < S and spent < args.cpu_budget:
+                rows = np.arange(done, min(S, done + 32))
+                t0 = time.perf_counter()
+                refs.append(att.attention_rows(Q, K, V, 1.0 / math.sqrt(D), True, 0, 0, rows))
+                spent += time.perf_counter() - t0
+                rows_all.append(rows)
+                done += rows.size
+        rows = np.concatenate(rows_all)
+        pairs = int(np.sum(rows + 1))
+        result["cpu_baseline"] = {"value": round(4.0 * pairs * D / spent / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": "causal rows 0..%d of head (0, 0), %.1f s (numpy fp64, BLAS limited to "
+                                            "%d threads)" % (done - 1, spent, threads)}
+        s = oracle.compare(got[rows], np.concatenate(refs))
+        result["parity"] = {"rows_checked": int(done), "max_abs": s["max_abs"], "rel_fro": s["rel_fro"],
+                            "pass": bool(oracle.within_tolerance(s, "bf16"))}
+    return result
+
+
 def sweep(args):
     """Ring depth S in 2, 3, 4 x 1, 2 or 4 producer waves on the 4096^3 fp32
     GEMM (256x128 tiles, 4 consumer waves; each point takes the deepest k tile
@@ -443,6 +520,8 @@ def main():
                    help="time the GEMM kernel without roles (every wave loads, barrier, computes) instead")
     p.add_argument("--no-ablation", action="store_true", help="skip the homogeneous_baseline measurement")
     p.add_argument("--sweep", action="store_true")
+    p.add_argument("--attention", action="store_true",
+                   help="attention forward (batch 4, 32 heads, 4096 x 4096, D 128) instead of the default step")
     p.add_argument("--moe", action="store_true",
                    help="the mixture-of-experts expert layer on the grouped GEMM instead of the default step")
     p.add_argument("--wait-stats", action="store_true",
@@ -457,6 +536,9 @@ def main():
         return
     if args.moe:
         print(json.dumps(run_moe(args)), flush=True)
+        return
+    if args.attention:
+        print(json.dumps(run_attention_bench(args)), flush=True)
         return
     print(json.dumps(run(args)), flush=True)
 

@@ -138,6 +138,31 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  */
 
 /*
+ * Scaled dot-product attention forward, the second consumer type: [WS] names
+ * attention beside GEMM among the kernels built on producer and consumer warps.
+ *   O[b, h, i, :] = sum_j P[i, j] V[b, h, j, :],
+ *   P[i, :] = softmax_j(scale * Q[b, h, i, :] . K[b, h, j, :])
+ * over the keys j the query may see: all of them, or with causal != 0 those
+ * with j <= i + (Skv - Sq) (the last query and the last key are aligned). A
+ * query that sees no key gets a row of zeros.
+ *   Q       batch x heads x Sq x D, K and V batch x heads x Skv x D: bf16 bit
+ *           patterns, dense row-major, 16-byte aligned.
+ *   O       batch x heads x Sq x D fp32, 4-byte aligned, not overlapping the
+ *           inputs.
+ *   D       64 or 128 (else WSG_EUNSUPPORTED); sizes >= 0; scale finite.
+ *   stages  ring slots of 64 keys (K and V tiles, 32 KiB per slot for
+ *           D = 128): 1 .. 4 for D = 128, 1 .. 9 for D = 64.
+ *   cfg     may be NULL; cfg->producer_waves (1, 2 or 4; 0 = default).
+ * Producer waves stream K and V tiles through the LDS ring; each consumer wave
+ * keeps 32 queries' rows in registers and runs an online softmax (running max
+ * and sum) with MFMAs for Q K^T and P V. Scores, softmax and accumulation are
+ * fp32; P is rounded to bf16 for the P V products.
+ */
+int attention_fwd(int64_t batch, int64_t heads, int64_t Sq, int64_t Skv, int64_t D, const uint16_t *Q,
+                  const uint16_t *K, const uint16_t *V, float *O, float scale, int causal, int stages,
+                  const wsg_config *cfg);
+
+/*
  * The configuration gemm_bias_relu_ex would launch for these arguments,
  * written to *out, after the same validation (returns its error code).
  * Writes the resolved tile and wave counts; no device work.
@@ -203,7 +228,8 @@ int wsg_check_device_status(void);
  *   out[3..5]   GEMM producers, empty waits  {waits, blocked, polls}
  *   out[6..8]   copy consumers, full waits
  *   out[9..11]  copy producers, empty waits
- *   out[12..15] zero
+ *   out[12..14] attention consumers, full waits
+ *   out[15]     zero
  * Counts accumulate over launches and across streams of one device until read.
  */
 int wsg_set_wait_stats(int enable);

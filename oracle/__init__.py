@@ -16,6 +16,8 @@ Contents
   * ringsim: a simulator of the full/empty ring protocol (oracle/ringsim.py).
   * grouped_gemm_bias_relu / grouped_gemm_bias_relu_rows: the same operator
     once per expert of a mixture-of-experts layer (oracle/grouped.py).
+  * attention.attention / attention.attention_rows: scaled dot-product
+    attention in fp64, the second consumer type (oracle/attention.py).
 """
 from __future__ import annotations
 

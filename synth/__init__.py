@@ -30,7 +30,7 @@ __all__ = [
     "GOLDEN", "MUL1", "MUL2", "WORKLOADS", "TENSOR_IDS",
     "seed_for", "splitmix64", "uniform_pm1", "normal_bf16_bits",
     "small_int_f32", "small_int_bf16_bits", "f32_to_bf16_bits_rne",
-    "bf16_bits_to_f32", "MOE", "moe_group_rows",
+    "bf16_bits_to_f32", "MOE", "moe_group_rows", "ATTENTION",
 ]
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -89,6 +89,14 @@ WORKLOADS = {
 MOE = dict(kind="grouped_gemm", dtype="bf16", experts=8, tokens=4096, top_k=2, K=4096, N=14336,
            dist="normal0.1", stages=3, id=6,
            name="bf16 grouped gemm+bias+relu, 8 experts, 4096 tokens top-2, K 4096, N 14336")
+
+
+# Attention forward, the second consumer type: batch 4, 32 heads, 4096
+# queries and keys, head dimension 128 (a common prefill shape; the pages name
+# none), Q, K, V i.i.d. N(0, 1) rounded to bf16, scale 1 / sqrt(D), 2-stage
+# ring; timed without and with the causal mask. Seeds use workload id 7.
+ATTENTION = dict(kind="attention", dtype="bf16", batch=4, heads=32, S=4096, D=128, dist="normal1", stages=2, id=7,
+                 name="bf16 attention forward, batch 4, 32 heads, 4096 queries and keys, head dim 128")
 
 
 def moe_group_rows(seed: int, tokens: int, experts: int, top_k: int) -> np.ndarray:

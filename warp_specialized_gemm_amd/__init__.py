@@ -8,7 +8,7 @@ exceptions. There is no fallback: if libwsg.so is missing or fails to load,
 importing this package raises.
 
 Names follow the C ABI: gemm_bias_relu, gemm_bias_relu_bf16,
-gemm_bias_relu_ex, grouped_gemm_bias_relu_ex, staged_copy, staged_copy_ex, resolve_config,
+gemm_bias_relu_ex, grouped_gemm_bias_relu_ex, attention_fwd, staged_copy, staged_copy_ex, resolve_config,
 check_device_status, set_stream, get_stream, last_error, version.
 """
 from __future__ import annotations
@@ -18,7 +18,8 @@ import os
 
 __all__ = [
     "WsgError", "Config", "lib", "library_path", "EXPORTS",
-    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "resolve_config",
+    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "attention_fwd",
+    "resolve_config",
     "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
     "set_stream", "get_stream",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
@@ -42,7 +43,7 @@ WSG_MAX_GROUPS = 64
 
 # every function include/wsg.h declares
 EXPORTS = (
-    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex",
+    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "attention_fwd",
     "wsg_gemm_resolve_config", "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
     "wsg_check_device_status", "wsg_set_wait_stats", "wsg_read_wait_stats", "wsg_version",
 )
@@ -81,6 +82,7 @@ def _load() -> ctypes.CDLL:
         "gemm_bias_relu_bf16": ([i64, i64, i64, vp, vp, vp, vp, ci], ci),
         "gemm_bias_relu_ex": ([ci, i64, i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
         "grouped_gemm_bias_relu_ex": ([ci, ci, ctypes.POINTER(i64), i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
+        "attention_fwd": ([i64, i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, ci, ci, cfgp], ci),
         "wsg_gemm_resolve_config": ([ci, i64, i64, i64, ci, cfgp, cfgp], ci),
         "staged_copy": ([vp, vp, ctypes.c_size_t, ci], ci),
         "staged_copy_ex": ([vp, vp, ctypes.c_size_t, ci, cfgp], ci),
@@ -237,6 +239,36 @@ def grouped_gemm_bias_relu_ex(A, B, bias, group_rows, C=None, stages: int = 4, c
     _raise_on(lib.grouped_gemm_bias_relu_ex(dtype, G, counts, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr(),
                                             C.data_ptr(), stages, _config(config)))
     return C
+
+
+def attention_fwd(Q, K, V, O=None, scale=None, causal: bool = False, stages: int = 2, config=None):
+    """O = softmax(scale * Q K^T [causal]) V; Q (batch, heads, Sq, D), K and V
+    (batch, heads, Skv, D) as bf16 tensors or their 16-bit patterns; fp32 O.
+    scale defaults to 1 / sqrt(D)."""
+    import math
+    import torch
+    ok = _bf16_ok()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+        if t.dtype not in ok:
+            raise TypeError("%s must have dtype in %s, got %s" % (name, ok, t.dtype))
+        if not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-d tensor (batch, heads, S, D)" % name)
+    Bn, H, Sq, D = Q.shape
+    if tuple(K.shape) != tuple(V.shape) or tuple(K.shape[:2]) != (Bn, H) or K.shape[3] != D:
+        raise ValueError("shape mismatch: Q %s, K %s, V %s" % (tuple(Q.shape), tuple(K.shape), tuple(V.shape)))
+    Skv = K.shape[2]
+    if O is None:
+        O = torch.empty((Bn, H, Sq, D), dtype=torch.float32, device=Q.device)
+    elif O.dtype != torch.float32 or tuple(O.shape) != (Bn, H, Sq, D) or not O.is_contiguous() or not O.is_cuda:
+        raise ValueError("O must be a contiguous float32 CUDA tensor of shape %s" % ((Bn, H, Sq, D),))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D) if D else 1.0
+    _use_current_stream()
+    _raise_on(lib.attention_fwd(Bn, H, Sq, Skv, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                float(scale), 1 if causal else 0, stages, _config(config)))
+    return O
 
 
 def resolve_config(dtype: int, M: int, N: int, K: int, stages: int = 4, config=None) -> dict:

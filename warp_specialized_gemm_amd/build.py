@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwsg.so")
-SOURCES = ["abi.hip", "staged_copy.hip", "gemm_bias_relu.hip"]
+SOURCES = ["abi.hip", "staged_copy.hip", "gemm_bias_relu.hip", "attention.hip"]
 ARCH = "gfx950"
 
 

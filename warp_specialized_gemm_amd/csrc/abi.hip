@@ -152,6 +152,42 @@ int grouped_impl(int dtype, int groups, const int64_t *group_rows, int64_t N, in
     return ok();
 }
 
+int attention_impl(int64_t batch, int64_t heads, int64_t Sq, int64_t Skv, int64_t D, const uint16_t *Q,
+                   const uint16_t *K, const uint16_t *V, float *O, float scale, int causal, int stages,
+                   const wsg_config *cfg) {
+    if (batch < 0 || heads < 0 || Sq < 0 || Skv < 0 || D < 0) return fail(WSG_EINVAL, "negative dimension");
+    if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(WSG_EINVAL, "scale must be finite");
+    if (D != 64 && D != 128) return fail(WSG_EUNSUPPORTED, "head dimension must be 64 or 128");
+    if (batch > kMaxDim || heads > kMaxDim || Sq > kMaxDim || Skv > kMaxDim)
+        return fail(WSG_EUNSUPPORTED, "dimension above 2^31 - 1");
+    const uint64_t BH = (uint64_t)batch * (uint64_t)heads;
+    if (BH > (uint64_t)kMaxDim) return fail(WSG_EUNSUPPORTED, "batch * heads above 2^31 - 1");
+    if (BH == 0 || Sq == 0) return ok();
+    if (BH * (uint64_t)Sq > kMaxElems / (uint64_t)D || BH * (uint64_t)Skv > kMaxElems / (uint64_t)D)
+        return fail(WSG_EUNSUPPORTED, "operand larger than 2^56 elements");
+    if (!Q || !O || (Skv > 0 && (!K || !V))) return fail(WSG_EINVAL, "null operand with a nonzero size");
+    if (((uintptr_t)Q % 16) || ((uintptr_t)K % 16) || ((uintptr_t)V % 16))
+        return fail(WSG_EINVAL, "Q, K and V must be 16-byte aligned");
+    if ((uintptr_t)O % 4) return fail(WSG_EINVAL, "O must be 4-byte aligned");
+    const size_t obytes = (size_t)(BH * (uint64_t)Sq * (uint64_t)D) * 4;
+    const size_t qbytes = (size_t)(BH * (uint64_t)Sq * (uint64_t)D) * 2;
+    const size_t kvbytes = (size_t)(BH * (uint64_t)Skv * (uint64_t)D) * 2;
+    if (overlaps(O, obytes, Q, qbytes) || overlaps(O, obytes, K, kvbytes) || overlaps(O, obytes, V, kvbytes))
+        return fail(WSG_EINVAL, "O overlaps an input");
+    wsg::LaunchCtx ctx;
+    int rc = device_info(&ctx.dev);
+    if (rc != WSG_OK) return rc;
+    ctx.stream = tl_stream;
+    ctx.wait_stats = tl_wait_stats;
+    std::string err;
+    rc = wsg::launch_attention(ctx, (int64_t)BH, Sq, Skv, D, Q, K, V, O, scale, causal, stages,
+                               cfg ? cfg->producer_waves : 0, &err);
+    if (rc != WSG_OK) return fail(rc, err);
+    return ok();
+}
+
 int copy_impl(const void *src, void *dst, size_t bytes, int stages, const wsg_config *cfg) {
     if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
     if (bytes == 0) return ok();
@@ -223,6 +259,12 @@ int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
 int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, int64_t N, int64_t K, const void *A,
                               const void *B, const void *bias, float *C, int stages, const wsg_config *cfg) {
     return grouped_impl(dtype, groups, group_rows, N, K, A, B, bias, C, stages, cfg);
+}
+
+int attention_fwd(int64_t batch, int64_t heads, int64_t Sq, int64_t Skv, int64_t D, const uint16_t *Q,
+                  const uint16_t *K, const uint16_t *V, float *O, float scale, int causal, int stages,
+                  const wsg_config *cfg) {
+    return attention_impl(batch, heads, Sq, Skv, D, Q, K, V, O, scale, causal, stages, cfg);
 }
 
 int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stages, const wsg_config *cfg,

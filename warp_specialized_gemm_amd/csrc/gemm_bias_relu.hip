@@ -47,15 +47,9 @@
 // as the baseline the specialization is measured against.
 #include "internal.hpp"
 #include "ring.hpp"
+#include "tiles.hpp"
 
 namespace wsg {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct GemmArgs {
     const unsigned char *A;
@@ -69,19 +63,11 @@ struct GemmArgs {
     unsigned long long *stats;  // wait statistics, or null
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2). Give each XCD a contiguous run of logical tiles, then walk those in
+// Each XCD takes a contiguous run of logical tiles (xcd_linear), walked in
 // groups of a few tile rows so the tiles resident on one XCD at a time share
-// rows of A and columns of B.
-constexpr int kXcds = 8;
-
-// kGroupRows tile rows per group: 8 for square tiles; for tall tiles fewer
-// rows (and so more columns) keep the A and B bytes a group touches balanced.
-__device__ __forceinline__ int xcd_linear(int bid, int total) {
-    const int x = bid % kXcds, i = bid / kXcds;
-    const int q = total / kXcds, r = total % kXcds;
-    return x * q + min(x, r) + i;
-}
+// rows of A and columns of B. kGroupRows tile rows per group: 8 for square
+// tiles; for tall tiles fewer rows (and so more columns) keep the A and B
+// bytes a group touches balanced.
 
 template <int kGroupRows>
 __device__ __forceinline__ void swizzle_tile(int L, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -170,110 +156,7 @@ __device__ __forceinline__ void resolve_tile(GroupedArgs &p, int &tm, int &tn) {
     swizzle_tile<kGroupRows>(L - t0, a.tiles_m, a.tiles_n, tm, tn);
 }
 
-// Kernel prologue for the ring's flags: zero the LDS flag words, then the
-// workgroup's first (and the specialized kernels' only) barrier.
-__device__ __forceinline__ LdsFlags init_flags(unsigned char *lds) {
-    if (threadIdx.x < kFlagBytes / 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0u;
-    __syncthreads();
-    return LdsFlags{lds_addr(lds), reinterpret_cast<const uint32_t *>(lds)};
-}
-
 __device__ __forceinline__ float relu_f32(float v) { return (v > 0.0f || v != v) ? v : 0.0f; }
-
-// XOR applied to the chunk index of row m (QPR chunks of 16 bytes per row)
-template <int QPR>
-__device__ __forceinline__ int row_swizzle(int m) {
-    if constexpr (QPR == 4) return (m >> 1) & 3;
-    else return m & 7;
-}
-
-// XOR applied to the chunk index of row k of a B slot (CPR chunks per row).
-// fp32 (CPR >= 16): the four k rows 4 apart that one b32 fragment read spans
-// land in different 64-byte bank groups. bf16: one transpose read has two
-// 16-lane groups (two column halves, 2 chunks each) over the same 4 rows;
-// XOR with 2r + 8(r & 1) (r = k mod 4) puts those 8 (row, chunk) pairs on 8
-// distinct 16-byte positions of a 128-byte span and all 16 pairs of both
-// groups on distinct positions of a 256-byte span. Rows of 8 chunks only get
-// the first part.
-template <int ES, int CPR>
-__device__ __forceinline__ int b_swizzle(int k) {
-    if constexpr (ES == 4) return ((k >> 2) & 3) << 2;
-    else if constexpr (CPR >= 16) return ((k & 3) << 1) | ((k & 1) << 3);
-    else return (k & 3) << 1;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// ----------------------------------------------------------------------------
-// A by LDS-DMA: BM rows x BK elements of ES bytes, QPR chunks per row.
-// ----------------------------------------------------------------------------
-template <int BM, int BK, int ES, int P>
-struct ADma {
-    static constexpr int EPC = 16 / ES;  // elements per chunk
-    static constexpr int QPR = BK / EPC;
-    static constexpr int CHUNKS = BM * QPR;
-    static constexpr int NL = CHUNKS / (64 * P);
-    static_assert(CHUNKS % (64 * P) == 0, "A chunks split evenly over producer waves");
-    uint32_t off[NL];
-    int kq[NL];
-    bool ok[NL];
-
-    __device__ __forceinline__ void init(int wave, int lane, int64_t K, int rows_valid) {
-#pragma unroll
-        for (int r = 0; r < NL; ++r) {
-            const int p = (r * P + wave) * 64 + lane;
-            const int m = p / QPR;
-            const int q = (p % QPR) ^ row_swizzle<QPR>(m);
-            off[r] = (uint32_t)m * (uint32_t)K * ES + (uint32_t)q * 16u;
-            kq[r] = q * EPC;
-            ok[r] = m < rows_valid;
-        }
-    }
-    __device__ __forceinline__ void issue(unsigned char *slot, int wave, const unsigned char *A_rows, int rows_valid,
-                                          int64_t K, int64_t k0) const {
-        const int64_t rec = ((int64_t)rows_valid * K - k0) * ES;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(A_rows + (size_t)k0 * ES, (uint32_t)min(rec, (int64_t)0x7FFFFFFF));
-#pragma unroll
-        for (int r = 0; r < NL; ++r)
-            lds_dma16(rs, slot + (r * P + wave) * 1024, (ok[r] && k0 + kq[r] < K) ? off[r] : kOobOffset);
-    }
-};
-
-// ----------------------------------------------------------------------------
-// B by LDS-DMA: BK rows x BN elements of ES bytes, chunks swizzled by k.
-// ----------------------------------------------------------------------------
-template <int BN, int BK, int ES, int P>
-struct BDma {
-    static constexpr int EPC = 16 / ES;
-    static constexpr int CPR = BN / EPC;  // chunks per row
-    static constexpr int CHUNKS = BK * CPR;
-    static constexpr int NL = CHUNKS / (64 * P);
-    static_assert(CHUNKS % (64 * P) == 0 && CPR >= (ES == 4 ? 16 : 8), "B chunks");
-    uint32_t off[NL];
-    int kk[NL];
-    bool ok[NL];
-
-    __device__ __forceinline__ void init(int wave, int lane, int64_t N, int64_t n0) {
-#pragma unroll
-        for (int r = 0; r < NL; ++r) {
-            const int p = (r * P + wave) * 64 + lane;
-            const int k = p / CPR;
-            const int c = (p % CPR) ^ b_swizzle<ES, CPR>(k);
-            off[r] = (uint32_t)k * (uint32_t)N * ES + (uint32_t)c * 16u;
-            kk[r] = k;
-            ok[r] = n0 + EPC * c < N;
-        }
-    }
-    __device__ __forceinline__ void issue(unsigned char *slotB, int wave, const unsigned char *B, int64_t N, int64_t K,
-                                          int64_t n0, int64_t k0) const {
-        const int64_t rec = (K * N - k0 * N - n0) * ES;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(B + (size_t)(k0 * N + n0) * ES, (uint32_t)min(rec, (int64_t)0x7FFFFFFF));
-#pragma unroll
-        for (int r = 0; r < NL; ++r)
-            lds_dma16(rs, slotB + (r * P + wave) * 1024, (ok[r] && k0 + kk[r] < K) ? off[r] : kOobOffset);
-    }
-};
 
 // ----------------------------------------------------------------------------
 // Register-staged loads with per-element masks, same slot layouts.

@@ -71,6 +71,13 @@ int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N
 int launch_grouped_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int groups, const int64_t *group_rows, int64_t N,
                         int64_t K, const void *A, const void *B, const void *bias, float *C, std::string *err);
 
+// Scaled dot-product attention forward over BH = batch * heads independent
+// heads (Q: BH x Sq x D, K and V: BH x Skv x D, bf16 bits; O fp32).
+// producers = 0 picks the default wave count.
+int launch_attention(const LaunchCtx &ctx, int64_t BH, int64_t Sq, int64_t Skv, int64_t D, const void *Q,
+                     const void *K, const void *V, float *O, float scale, int causal, int stages, int producers,
+                     std::string *err);
+
 int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo &dev, CopyPlan *plan,
               std::string *err);
 int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, void *dst, size_t bytes,

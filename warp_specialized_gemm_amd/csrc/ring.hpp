@@ -47,12 +47,14 @@ constexpr int kStatGemmConsumer = 0;  // full waits of GEMM consumers (early fla
 constexpr int kStatGemmProducer = 3;  // empty waits of GEMM producers
 constexpr int kStatCopyConsumer = 6;
 constexpr int kStatCopyProducer = 9;
+constexpr int kStatAttnConsumer = 12;  // full waits of attention consumers
 constexpr int kStatWords = 16;
 
 // device status word bits
 constexpr unsigned kStatusTimeout = 1u;
 constexpr unsigned kStatusCopy = 2u;
 constexpr unsigned kStatusGemm = 4u;
+constexpr unsigned kStatusAttention = 8u;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
