@@ -41,8 +41,11 @@ PEAK_TFLOPS = {"fp32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gemm": ["warp_specialized_gemm_amd/csrc/gemm_bias_relu.hip", "warp_specialized_gemm_amd/csrc/ring.hpp"],
+    "gemm": ["warp_specialized_gemm_amd/csrc/gemm_bias_relu.hip", "warp_specialized_gemm_amd/csrc/ring.hpp",
+             "warp_specialized_gemm_amd/csrc/tiles.hpp"],
     "copy": ["warp_specialized_gemm_amd/csrc/staged_copy.hip", "warp_specialized_gemm_amd/csrc/ring.hpp"],
+    "attention": ["warp_specialized_gemm_amd/csrc/attention.hip", "warp_specialized_gemm_amd/csrc/ring.hpp",
+                  "warp_specialized_gemm_amd/csrc/tiles.hpp"],
 }
 
 
@@ -425,10 +428,11 @@ def run_attention_bench(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w["name"], "batch": Bn, "heads": H, "Sq": S, "Skv": S, "D": D, "stages": stages,
-                   "producer_waves": args.producers or 2, "consumer_waves": 4, "queries_per_workgroup": 128,
+                   "producer_waves": args.producers or 1, "consumer_waves": 4, "queries_per_workgroup": 128,
                    "keys_per_slot": 64, "input": "N(0,1) rounded to bf16, scale 1/sqrt(D)"},
         "roofline": {"bound": "mfma", "achieved": round(flops / kern / 1e12, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(flops / kern / 1e12 / peak, 4), "traffic": None,
+                     "frac": round(flops / kern / 1e12 / peak, 4),
+                     "traffic": measured_traffic("attention_d128_noncausal", "attention"),
                      "kernel_ms": round(kern * 1e3, 4), "kernel_ms_min": round(kmin * 1e3, 4)},
     }
     cf, cw, ck, cm = out[True]

@@ -93,9 +93,9 @@ MOE = dict(kind="grouped_gemm", dtype="bf16", experts=8, tokens=4096, top_k=2, K
 
 # Attention forward, the second consumer type: batch 4, 32 heads, 4096
 # queries and keys, head dimension 128 (a common prefill shape; the pages name
-# none), Q, K, V i.i.d. N(0, 1) rounded to bf16, scale 1 / sqrt(D), 2-stage
+# none), Q, K, V i.i.d. N(0, 1) rounded to bf16, scale 1 / sqrt(D), 3-stage
 # ring; timed without and with the causal mask. Seeds use workload id 7.
-ATTENTION = dict(kind="attention", dtype="bf16", batch=4, heads=32, S=4096, D=128, dist="normal1", stages=2, id=7,
+ATTENTION = dict(kind="attention", dtype="bf16", batch=4, heads=32, S=4096, D=128, dist="normal1", stages=3, id=7,
                  name="bf16 attention forward, batch 4, 32 heads, 4096 queries and keys, head dim 128")
 
 

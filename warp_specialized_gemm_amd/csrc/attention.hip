@@ -126,7 +126,8 @@ __global__ void __launch_bounds__((P + 4) * 64) attention_kernel(AttnArgs a) {
     const int li = lane & 31, h = lane >> 5, ip = lane & 15;
     const int64_t qrow = q0 + 32 * cw + li;
     const bool qvalid = qrow < Sq;
-    const int64_t last_key = qrow + (Skv - Sq);  // causal: the last key this query sees
+    const int64_t last_key = qrow + (Skv - Sq);              // causal: the last key this query sees
+    const int64_t wave_last_key = q0 + 32 * cw + (Skv - Sq);  // the same for the wave's first query
 
     // Q^T as the B operand: lane (li, h) holds d = 16 s + 8 h .. + 7 of its query
     bf16x8 qf[DS];
@@ -192,30 +193,27 @@ __global__ void __launch_bounds__((P + 4) * 64) attention_kernel(AttnArgs a) {
                 sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
             }
         }
-        // V^T fragments of the whole tile (the slot is released once they landed)
-        bf16x8 vf[KS][DB];
+        // online softmax over this tile's keys, in base 2 (scores times
+        // scale * log2 e); masked keys are -inf. Only tiles that reach past
+        // Skv or past the causal limit of the wave's first query need the
+        // mask (a wave-uniform test), so interior tiles skip it.
+        const bool edge = k0 + BKV > Skv || (a.causal && k0 + BKV - 1 > wave_last_key);
+        if (edge) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int b = 0; b < KB; ++b)
 #pragma unroll
-            for (int c = 0; c < DB; ++c) {
-                const unsigned char *p = slotV + v_row + 16 * ks * D * 2 + v_col[c];
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 8 * D * 2));
-                vf[ks][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-
-        // online softmax over this tile's keys, in base 2; masked keys are -inf
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t key = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = key < Skv && (!a.causal || key <= last_key);
+                    sc[b][r] = vis ? sc[b][r] : -__builtin_inff();
+                }
+        }
         float mt = -__builtin_inff();
 #pragma unroll
         for (int b = 0; b < KB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t key = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool vis = key < Skv && (!a.causal || key <= last_key);
-                sc[b][r] = vis ? sc[b][r] * sl2 : -__builtin_inff();
-                mt = fmaxf(mt, sc[b][r]);
-            }
-        mt = lane_max(mt);
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[b][r]);
+        mt = lane_max(mt) * sl2;
         const float m_new = fmaxf(m_run, mt);
         const bool none = m_new == -__builtin_inff();  // no visible key so far
         const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -225,7 +223,7 @@ __global__ void __launch_bounds__((P + 4) * 64) attention_kernel(AttnArgs a) {
         for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = none ? 0.0f : __builtin_amdgcn_exp2f(sc[b][r] - m_new);
+                const float p = none ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], sl2, -m_new));
                 rs += p;
                 pf[2 * b + (r >> 3)][r & 7] = (__bf16)p;
             }
@@ -237,18 +235,27 @@ __global__ void __launch_bounds__((P + 4) * 64) attention_kernel(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_o[c][r] *= alpha;
 
+        // O^T += V^T P^T, V^T fragments read one key step at a time
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 vf[DB];
+#pragma unroll
+            for (int c = 0; c < DB; ++c) {
+                const unsigned char *p = slotV + v_row + 16 * ks * D * 2 + v_col[c];
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 8 * D * 2));
+                vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int c = 0; c < DB; ++c)
+                acc_o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], pf[ks], acc_o[c], 0, 0, 0);
+        }
         wait_lgkm0();  // every read of the slot has landed
         fl.arrive_empty(cs);
         if (++cs == S) {
             cs = 0;
             ++lap;
         }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int c = 0; c < DB; ++c)
-                acc_o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][c], pf[ks], acc_o[c], 0, 0, 0);
     }
     publish_tally(a.stats ? a.stats + kStatAttnConsumer : nullptr, tally);
 
@@ -274,7 +281,7 @@ struct AttnVariant {
 
 // First match per head dimension is the default.
 const AttnVariant kAttnVariants[] = {
-    WSG_ATTN(128, 2), WSG_ATTN(128, 1), WSG_ATTN(128, 4), WSG_ATTN(64, 1), WSG_ATTN(64, 2),
+    WSG_ATTN(128, 1), WSG_ATTN(128, 2), WSG_ATTN(128, 4), WSG_ATTN(64, 1), WSG_ATTN(64, 2),
 };
 
 }  // namespace
