@@ -67,10 +67,12 @@ __global__ void __launch_bounds__((P + 4) * 64) attention_kernel(AttnArgs a) {
     const LdsFlags fl = init_flags(lds);
 
     // consecutive logical tiles (one XCD) are the query tiles of one head,
-    // so that head's K and V stay in that XCD's L2
+    // so that head's K and V stay in that XCD's L2; with the causal mask the
+    // last query tiles see the most keys, so they go first
     const int L = xcd_linear(blockIdx.x, a.tiles);
     const int64_t bh = L / a.q_tiles;
-    const int64_t q0 = (int64_t)(L % a.q_tiles) * kAttnQueries;
+    const int qt = L % a.q_tiles;
+    const int64_t q0 = (int64_t)(a.causal ? a.q_tiles - 1 - qt : qt) * kAttnQueries;
     const int64_t Sq = a.Sq, Skv = a.Skv;
     int64_t kv_end = Skv;
     if (a.causal) kv_end = max((int64_t)0, min(Skv, min(q0 + kAttnQueries, Sq) + (Skv - Sq)));
