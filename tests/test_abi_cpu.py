@@ -85,6 +85,42 @@ def test_invalid_arguments_rejected_before_any_device_call(wsg):
     assert L.staged_copy(0x1000, 0x9000, 64, 0) == wsg.WSG_EINVAL
 
 
+def test_grouped_and_attention_arguments_rejected_before_any_device_call(wsg):
+    L = wsg.lib
+    rows = lambda *r: (ctypes.c_int64 * max(1, len(r)))(*r)  # noqa: E731
+    A, B, b, C = 0x100000, 0x200000, 0x300000, 0x400000
+    g = L.grouped_gemm_bias_relu_ex
+    assert g(wsg.WSG_FP32, 0, rows(), 8, 16, A, B, b, C, 2, None) == wsg.WSG_EINVAL
+    assert g(wsg.WSG_FP32, wsg.WSG_MAX_GROUPS + 1, rows(*[1] * 65), 8, 16, A, B, b, C, 2, None) == \
+        wsg.WSG_EUNSUPPORTED
+    assert g(wsg.WSG_FP32, 2, None, 8, 16, A, B, b, C, 2, None) == wsg.WSG_EINVAL
+    assert g(wsg.WSG_FP32, 2, rows(3, -1), 8, 16, A, B, b, C, 2, None) == wsg.WSG_EINVAL
+    assert g(wsg.WSG_FP32, 2, rows(3, 1), 8, 16, A, B, b, C, 0, None) == wsg.WSG_EINVAL
+    assert g(7, 2, rows(3, 1), 8, 16, A, B, b, C, 2, None) == wsg.WSG_EINVAL
+    # C inside the second expert's block of B (2 x 16 x 8 floats from B)
+    assert g(wsg.WSG_FP32, 2, rows(3, 1), 8, 16, A, B, b, B + 16 * 8 * 4 + 64, 2, None) == wsg.WSG_EINVAL
+    assert "overlap" in wsg.last_error()
+    # no rows, or no columns: nothing to do
+    assert g(wsg.WSG_FP32, 3, rows(0, 0, 0), 8, 16, None, None, None, None, 2, None) == wsg.WSG_OK
+    assert g(wsg.WSG_FP32, 2, rows(3, 1), 0, 16, None, None, None, None, 2, None) == wsg.WSG_OK
+
+    a = L.attention_fwd
+    Q, K, V, O = 0x100000, 0x200000, 0x300000, 0x400000
+    assert a(-1, 1, 4, 4, 128, Q, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EINVAL
+    assert a(1, 1, 4, 4, 96, Q, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EUNSUPPORTED
+    assert a(1, 1, 4, 4, 128, Q, K, V, O, float("nan"), 0, 2, None) == wsg.WSG_EINVAL
+    assert a(1, 1, 4, 4, 128, Q, K, V, O, float("inf"), 0, 2, None) == wsg.WSG_EINVAL
+    assert a(1, 1, 4, 4, 128, Q, K, V, O, 1.0, 0, 0, None) == wsg.WSG_EINVAL
+    assert a(1, 1, 4, 4, 128, None, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EINVAL
+    assert a(1, 1, 4, 4, 128, Q + 2, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EINVAL  # Q not 16-byte aligned
+    assert a(1, 1, 4, 4, 128, Q, K, V, Q + 64, 1.0, 0, 2, None) == wsg.WSG_EINVAL  # O overlaps Q
+    assert "overlap" in wsg.last_error()
+    assert a(1, 1 << 31, 4, 4, 128, Q, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EUNSUPPORTED
+    # no heads or no queries: nothing to do; no keys needs no K or V
+    assert a(0, 4, 4, 4, 128, None, None, None, None, 1.0, 0, 2, None) == wsg.WSG_OK
+    assert a(1, 4, 0, 4, 128, None, None, None, None, 1.0, 1, 2, None) == wsg.WSG_OK
+
+
 def test_stream_is_thread_local(wsg):
     import threading
     wsg.lib.wsg_set_stream(ctypes.c_void_p(0x1234))
