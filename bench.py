@@ -17,6 +17,9 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
   cpu_baseline         = the CPU oracle on a bounded sample of the same GEMM
   homogeneous_baseline = the same GEMM, tile and ring depth on the kernel
                          without roles (every wave loads, barrier, computes)
+  vendor_library       = the same GEMM through torch (relu_(addmm), hipBLASLt)
+                         in the input dtype, for context; two launches, so
+                         its figure includes a separate ReLU pass
   copy.plain_device_copy = torch's own device-to-device copy of the same
                          buffers, the bandwidth a plain copy kernel reaches
 Options select other workloads (--workload 4: ragged fp32, --workload 5:
@@ -245,6 +248,28 @@ def run(args):
             del dC_h
         except wsg.WsgError as e:
             result["homogeneous_baseline"] = {"error": str(e)}
+
+    if not args.no_vendor:
+        # the vendor library (hipBLASLt through torch) on the same operands, for
+        # context: relu(addmm) in the input dtype, so its output is bf16 when the
+        # inputs are (half the C bytes this library writes)
+        tdt_v = torch.float32 if dtype == "fp32" else torch.bfloat16
+        vA, vB, vb = dA.view(tdt_v), dB.view(tdt_v), dbias.view(tdt_v)
+        prev_tf32 = torch.backends.cuda.matmul.allow_tf32
+        torch.backends.cuda.matmul.allow_tf32 = False
+        try:
+            vendor = lambda: torch.relu_(torch.addmm(vb, vA, vB))  # noqa: E731
+            for _ in range(args.warmup):
+                vendor()
+            v_wall, v_kern, _ = time_region(torch, vendor, args.steps)
+        finally:
+            torch.backends.cuda.matmul.allow_tf32 = prev_tf32
+        result["vendor_library"] = {
+            "op": "torch.relu_(torch.addmm(bias, A, B)), %s in and out" % ("fp32" if dtype == "fp32" else "bf16"),
+            "value": round(flops * args.steps / v_wall / 1e12, 3), "unit": "TFLOP/s",
+            "launch_tflops": round(flops / v_kern / 1e12, 3),
+            "ours_over_vendor": round(v_kern / g_kern, 4),
+        }
 
     if copy_src is not None:
         c_wall, c_kern, c_min = time_region(torch, copy, args.steps)
@@ -523,6 +548,8 @@ def main():
     p.add_argument("--homogeneous", action="store_true",
                    help="time the GEMM kernel without roles (every wave loads, barrier, computes) instead")
     p.add_argument("--no-ablation", action="store_true", help="skip the homogeneous_baseline measurement")
+    p.add_argument("--no-vendor", action="store_true",
+                   help="skip the vendor_library leg (the same GEMM through torch.addmm, for context)")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--attention", action="store_true",
                    help="attention forward (batch 4, 32 heads, 4096 x 4096, D 128) instead of the default step")
