@@ -72,8 +72,9 @@ WORKLOADS = {
     3: dict(kind="gemm", dtype="fp32", M=4096, N=4096, K=4096, dist="uniform",
             stages=2, stage_sweep=(2, 3, 4),
             name="fp32 gemm+bias+relu 4096x4096x4096"),
+    # 2 stages: a ring of 256x128x32 tiles (a 4-stage ring only holds k = 16)
     4: dict(kind="gemm", dtype="fp32", M=3000, N=5000, K=4100, dist="uniform",
-            stages=4,
+            stages=2,
             name="fp32 gemm+bias+relu ragged 3000x5000x4100"),
     5: dict(kind="gemm", dtype="bf16", M=8192, N=8192, K=8192, dist="normal0.1",
             stages=4,

@@ -203,10 +203,11 @@ def test_full_size_workload_sampled(gpu, wid):
     assert 0.4 < frac_zero < 0.6, frac_zero  # symmetric pre-activations: about half clamp to 0
 
 
-def test_ragged_full_size_integer_bit_exact(gpu):
+@pytest.mark.parametrize("stages", [2, 4])  # 256x128x32 and 256x128x16 tiles
+def test_ragged_full_size_integer_bit_exact(gpu, stages):
     M, N, K = 3000, 5000, 4100
     A, B, bias = int_case(4444, M, N, K)
-    C = run_gemm(gpu, A, B, bias, stages=4, guards=False)
+    C = run_gemm(gpu, A, B, bias, stages=stages, guards=False)
     rows = _sampled_rows(M, 10, 5)
     assert np.array_equal(C[rows].astype(np.float64), oracle.gemm_bias_relu_rows(A, B, bias, rows))
     # last tile row and column (56 rows, 8 columns past the last full tile)
