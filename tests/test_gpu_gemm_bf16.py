@@ -103,6 +103,9 @@ VARIANTS = [
     dict(BM=256, BN=128, BK=64, producer_waves=4, consumer_waves=4, group_k=16),
     dict(BM=256, BN=128, BK=32, producer_waves=2, consumer_waves=4, group_k=32),
     dict(BM=256, BN=128, BK=32, producer_waves=4, consumer_waves=4, group_k=16),
+    # 48-deep k tiles: rows of 6 chunks, rotation swizzle; K = 296 leaves an 8-deep last tile
+    dict(BM=256, BN=128, BK=48, producer_waves=4, consumer_waves=4, group_k=16),
+    dict(BM=256, BN=128, BK=48, producer_waves=2, consumer_waves=4, group_k=16),
 ]
 
 

@@ -22,7 +22,7 @@ F32_TILES = [dict(BM=256, BN=128, BK=32, consumer_waves=4), dict(BM=256, BN=128,
              dict(BM=128, BN=128, BK=32, consumer_waves=4), dict(BM=64, BN=64, BK=16, consumer_waves=4)]
 BF16_TILES = [dict(BM=256, BN=128, BK=64, consumer_waves=4), dict(BM=256, BN=128, BK=64, consumer_waves=8),
               dict(BM=256, BN=128, BK=32, consumer_waves=4), dict(BM=128, BN=128, BK=32, consumer_waves=4),
-              dict(BM=64, BN=64, BK=32, consumer_waves=4)]
+              dict(BM=64, BN=64, BK=32, consumer_waves=4), dict(BM=256, BN=128, BK=48, consumer_waves=4)]
 
 
 def _h(cfg):

@@ -171,7 +171,7 @@ __device__ __forceinline__ void a_general(unsigned char *slotA, int wave, int la
     for (int r = 0; r < NL; ++r) {
         const int p = (r * P + wave) * 64 + lane;
         const int m = p / QPR;
-        const int q = (p % QPR) ^ row_swizzle<QPR>(m);
+        const int q = chunk_of<QPR>(p % QPR, chunk_param<QPR>(m));
         u32x4 v;
         if constexpr (ES == 4) {
             const float *Af = reinterpret_cast<const float *>(A);
@@ -747,7 +747,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
     for (int i = 0; i < FM; ++i) {
         const int row = wr * WTM + 32 * i + li;
         a_off[i] = row * QPR * 16;
-        a_swz[i] = row_swizzle<QPR>(row);
+        a_swz[i] = chunk_param<QPR>(row);
     }
     // B: in 16-lane group g16 = lane / 16 (k half h = g16 / 2, column half
     // g16 % 2), lane i' = lane % 16 points at columns 4 * (i' % 4) .. + 3 of k
@@ -776,7 +776,7 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
             const int c = 2 * step + h;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                f.a[ks][i] = *reinterpret_cast<const bf16x8 *>(slot + a_off[i] + ((c ^ a_swz[i]) << 4));
+                f.a[ks][i] = *reinterpret_cast<const bf16x8 *>(slot + a_off[i] + (chunk_at<QPR>(c, a_swz[i]) << 4));
             const unsigned char *slotB = slot + A_BYTES + b_row + 16 * step * BN * 2;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -882,7 +882,8 @@ const GemmVariant kGemmVariants[] = {
     // TFLOP/s for 4 / 2 producers at S = 2, 1019 / 1007 at S = 3 and 846 / 840
     // at S = 4 (k = 32 tiles); with one producer, consumers found the next
     // tile unpublished at 41% of their waits.
-    WSG_BF(256, 128, 64, 4, 2, 2, true, 32),  WSG_BF(256, 128, 32, 4, 2, 2, true, 32),
+    WSG_BF(256, 128, 64, 4, 2, 2, true, 32),  WSG_BF(256, 128, 48, 4, 2, 2, true, 16),
+    WSG_BF(256, 128, 48, 2, 2, 2, true, 16),  WSG_BF(256, 128, 32, 4, 2, 2, true, 32),
     WSG_BF(256, 128, 64, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 2, 2, 2, true, 16),
     WSG_BF(256, 128, 32, 2, 2, 2, true, 32),  WSG_BF(256, 128, 64, 1, 2, 2, true, 32),
     WSG_BF(256, 128, 32, 1, 2, 2, true, 32),  WSG_BF(256, 128, 32, 1, 2, 2, true, 16),
@@ -893,6 +894,7 @@ const GemmVariant kGemmVariants[] = {
     WSG_BF(128, 128, 32, 1, 2, 2, false, 16), WSG_BF(64, 64, 32, 1, 2, 2, false, 16),
     // bf16, homogeneous
     WSG_BF(256, 128, 64, 0, 2, 2, true, 32),  WSG_BF(256, 128, 64, 0, 4, 2, true, 32),
+    WSG_BF(256, 128, 48, 0, 2, 2, true, 16),
     WSG_BF(256, 128, 32, 0, 2, 2, true, 32),  WSG_BF(128, 128, 32, 0, 2, 2, true, 16),
     WSG_BF(64, 64, 32, 0, 2, 2, true, 16),
 };

@@ -41,6 +41,35 @@ __device__ __forceinline__ int row_swizzle(int m) {
     else return m & 7;
 }
 
+// Slot position of logical 16-byte chunk q of row m, through a per-row
+// parameter. Rows of a power-of-two chunk count: XOR with row_swizzle. Rows of
+// 6 chunks (a 48-deep bf16 k tile): rotation by (m / 8) mod 6, which puts the
+// 16 consecutive rows one read pass covers on 16 distinct 16-byte positions
+// of a 256-byte bank span (96-byte rows repeat their bank offset every 8 rows).
+template <int QPR>
+__device__ __forceinline__ int chunk_param(int m) {
+    if constexpr (QPR == 6) return (m >> 3) % 6;
+    else return row_swizzle<QPR>(m);
+}
+template <int QPR>
+__device__ __forceinline__ int chunk_at(int q, int param) {  // logical -> slot
+    if constexpr (QPR == 6) {
+        const int s = q + param;
+        return s >= 6 ? s - 6 : s;
+    } else {
+        return q ^ param;
+    }
+}
+template <int QPR>
+__device__ __forceinline__ int chunk_of(int pq, int param) {  // slot -> logical
+    if constexpr (QPR == 6) {
+        const int s = pq - param;
+        return s < 0 ? s + 6 : s;
+    } else {
+        return pq ^ param;
+    }
+}
+
 // XOR applied to the chunk index of row k of a B slot (CPR chunks per row).
 // fp32 (CPR >= 16): the four k rows 4 apart that one b32 fragment read spans
 // land in different 64-byte bank groups. bf16: one transpose read has two
@@ -77,7 +106,7 @@ struct ADma {
         for (int r = 0; r < NL; ++r) {
             const int p = (r * P + wave) * 64 + lane;
             const int m = p / QPR;
-            const int q = (p % QPR) ^ row_swizzle<QPR>(m);
+            const int q = chunk_of<QPR>(p % QPR, chunk_param<QPR>(m));
             off[r] = (uint32_t)m * (uint32_t)K * ES + (uint32_t)q * 16u;
             kq[r] = q * EPC;
             ok[r] = m < rows_valid;
