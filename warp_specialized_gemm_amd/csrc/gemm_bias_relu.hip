@@ -20,9 +20,9 @@
 //   register-staged producer with per-element masks and the same slot layout.
 //
 // Slot layout: A as BM rows of BK elements, 16-byte chunks XOR-swizzled
-// within a row so that consecutive rows reading the same chunk index hit
-// distinct banks; B as BK rows of BN elements (its natural layout), chunks
-// XOR-swizzled by k.
+// within a row (rotated, for the 6-chunk rows of a 48-deep bf16 tile) so that
+// consecutive rows reading the same chunk index hit distinct banks; B as BK
+// rows of BN elements (its natural layout), chunks XOR-swizzled by k.
 //
 // Consumers (one wave per SIMD in the default tiles: 2 x 2 waves of 128 x 64)
 //   fp32: v_mfma_f32_16x16x4_f32. Over a 16-deep k group, lane group q
