@@ -44,6 +44,7 @@ struct AttnArgs {
 
 constexpr int kAttnQueries = 128;  // per workgroup: 4 consumer waves x 32
 constexpr int kAttnKeys = 64;      // per ring slot
+constexpr int kKAhead = 4;         // K fragment reads in flight ahead of the score MFMAs
 
 __device__ __forceinline__ float lane_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 __device__ __forceinline__ float lane_sum(float v) { return v + __shfl_xor(v, 32); }
@@ -186,14 +187,30 @@ __global__ void __launch_bounds__((P + 4) * 64) attention_kernel(AttnArgs a) {
         for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[b][r] = 0.0f;
+        // K fragments are read kKAhead MFMAs ahead of their use: left to
+        // itself the scheduler keeps two in flight, and each pair of MFMAs
+        // waited a whole LDS round trip (measured on MI355X: +2.4% non-causal,
+        // +3.2% causal with 4 ahead; 6 or 8 gained no more).
+        {
+            bf16x8 kf[DS][KB];
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-            const int c = 2 * s + h;
+            for (int s = 0; s < DS; ++s)
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(slot + k_off[b] + ((c ^ k_swz[b]) << 4));
-                sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[b], 0, 0, 0);
+                for (int b = 0; b < KB; ++b)
+                    kf[s][b] = *reinterpret_cast<const bf16x8 *>(slot + k_off[b] + (((2 * s + h) ^ k_swz[b]) << 4));
+#pragma unroll
+            for (int s = 0; s < DS; ++s)
+#pragma unroll
+                for (int b = 0; b < KB; ++b)
+                    sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][b], qf[s], sc[b], 0, 0, 0);
+            constexpr int NK = DS * KB, AH = kKAhead < NK ? kKAhead : NK;
+            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // AH LDS reads first
+#pragma unroll
+            for (int i = 0; i < NK - AH; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // and one read
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);  // the last AH MFMAs
         }
         // online softmax over this tile's keys, in base 2 (scores times
         // scale * log2 e); masked keys are -inf. Only tiles that reach past
