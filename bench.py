@@ -438,7 +438,10 @@ def run_attention_bench(args):
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()  # noqa: E731
     dQ, dK, dV = dev(Q), dev(K), dev(V)
     dO = torch.empty((Bn, H, S, D), dtype=torch.float32, device="cuda")
-    config = dict(producer_waves=args.producers) if args.producers else None
+    # the library's default for head dimension 128: one producer and seven consumer waves
+    producers = args.producers or 1
+    consumers = args.consumers or (7 if producers == 1 and D == 128 else 4)
+    config = dict(producer_waves=producers, consumer_waves=consumers)
     peak = PEAK_TFLOPS["bf16"]
     out = {}
     for causal in (False, True):
@@ -458,7 +461,7 @@ def run_attention_bench(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w["name"], "batch": Bn, "heads": H, "Sq": S, "Skv": S, "D": D, "stages": stages,
-                   "producer_waves": args.producers or 1, "consumer_waves": 4, "queries_per_workgroup": 128,
+                   "producer_waves": producers, "consumer_waves": consumers, "queries_per_workgroup": 32 * consumers,
                    "keys_per_slot": 64, "input": "N(0,1) rounded to bf16, scale 1/sqrt(D)"},
         "roofline": {"bound": "mfma", "achieved": round(flops / kern / 1e12, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(flops / kern / 1e12 / peak, 4),

@@ -152,7 +152,9 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  *   D       64 or 128 (else WSG_EUNSUPPORTED); sizes >= 0; scale finite.
  *   stages  ring slots of 64 keys (K and V tiles, 32 KiB per slot for
  *           D = 128): 1 .. 4 for D = 128, 1 .. 9 for D = 64.
- *   cfg     may be NULL; cfg->producer_waves (1, 2 or 4; 0 = default).
+ *   cfg     may be NULL; cfg->producer_waves (1, 2 or 4; 0 = default) and
+ *           cfg->consumer_waves (4, or 7 with one producer for D = 128;
+ *           0 = default). Other combinations: WSG_EUNSUPPORTED.
  * Producer waves stream K and V tiles through the LDS ring; each consumer wave
  * keeps 32 queries' rows in registers and runs an online softmax (running max
  * and sum) with MFMAs for Q K^T and P V. Scores, softmax and accumulation are

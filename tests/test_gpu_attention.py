@@ -86,6 +86,29 @@ def test_ring_depths_and_producers(gpu, stages, producers):
     check(O, att.attention(Q, K, V, 1.0 / math.sqrt(128), True))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == 128], ids=lambda s: "x".join(map(str, s)))
+def test_seven_consumers(gpu, shape, causal):
+    """224 queries per workgroup (7 consumer waves, one of which arrives twice on the empty flags)."""
+    Bn, H, Sq, Skv, D = shape
+    Q, K, V = case(sum(shape) * 11 + causal, Bn, H, Sq, Skv, D)
+    cfg = dict(producer_waves=1, consumer_waves=7)
+    O = run_attention(gpu, Q, K, V, causal, stages=3, config=cfg)
+    check(O, att.attention(Q, K, V, 1.0 / math.sqrt(D), causal))
+
+
+def test_seven_consumers_same_bits_as_four(gpu):
+    """Each query's arithmetic does not depend on how queries are grouped into workgroups."""
+    Q, K, V = case(800, 2, 2, 500, 700, 128)
+    for causal in (False, True):
+        four = run_attention(gpu, Q, K, V, causal, stages=3, config=dict(producer_waves=1, consumer_waves=4),
+                             guards=False)
+        for stages in (1, 2, 3, 4):
+            seven = run_attention(gpu, Q, K, V, causal, stages=stages,
+                                  config=dict(producer_waves=1, consumer_waves=7), guards=False)
+            assert np.array_equal(seven.view(np.uint32), four.view(np.uint32))
+
+
 def test_scale_and_large_scores(gpu):
     """Scores far from 1: the running max keeps the exponentials in range."""
     Q, K, V = case(500, 1, 1, 96, 300, 64)
@@ -127,6 +150,14 @@ def test_errors(gpu):
     assert e.value.code == gpu.WSG_EINVAL
     with pytest.raises(gpu.WsgError) as e:
         gpu.attention_fwd(q, q, q, config=dict(producer_waves=3))
+    assert e.value.code == gpu.WSG_EUNSUPPORTED
+    for cfg in (dict(producer_waves=2, consumer_waves=7), dict(consumer_waves=5)):
+        with pytest.raises(gpu.WsgError) as e:
+            gpu.attention_fwd(q, q, q, config=cfg)
+        assert e.value.code == gpu.WSG_EUNSUPPORTED
+    q64 = q[..., :64].contiguous()
+    with pytest.raises(gpu.WsgError) as e:
+        gpu.attention_fwd(q64, q64, q64, config=dict(consumer_waves=7))
     assert e.value.code == gpu.WSG_EUNSUPPORTED
     buf = torch.zeros(64 * 128 + 8, dtype=torch.int16, device="cuda")
     mis = buf[1:1 + 64 * 128].view(1, 1, 64, 128)  # 2-byte offset

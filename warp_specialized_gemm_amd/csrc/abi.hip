@@ -183,7 +183,7 @@ int attention_impl(int64_t batch, int64_t heads, int64_t Sq, int64_t Skv, int64_
     ctx.wait_stats = tl_wait_stats;
     std::string err;
     rc = wsg::launch_attention(ctx, (int64_t)BH, Sq, Skv, D, Q, K, V, O, scale, causal, stages,
-                               cfg ? cfg->producer_waves : 0, &err);
+                               cfg ? cfg->producer_waves : 0, cfg ? cfg->consumer_waves : 0, &err);
     if (rc != WSG_OK) return fail(rc, err);
     return ok();
 }

@@ -73,10 +73,10 @@ int launch_grouped_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int groups, 
 
 // Scaled dot-product attention forward over BH = batch * heads independent
 // heads (Q: BH x Sq x D, K and V: BH x Skv x D, bf16 bits; O fp32).
-// producers = 0 picks the default wave count.
+// producers = 0 / consumers = 0 pick the default wave counts.
 int launch_attention(const LaunchCtx &ctx, int64_t BH, int64_t Sq, int64_t Skv, int64_t D, const void *Q,
                      const void *K, const void *V, float *O, float scale, int causal, int stages, int producers,
-                     std::string *err);
+                     int consumers, std::string *err);
 
 int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo &dev, CopyPlan *plan,
               std::string *err);

@@ -130,13 +130,15 @@ __device__ __forceinline__ void publish_tally(unsigned long long *stats, const W
     atomicAdd(stats + 2, (unsigned long long)t.polls);
 }
 
-// One arrival of the calling wave: lane 0 adds 1. The caller has already
+// One arrival of the calling wave: lane 0 adds n (1 unless a wave stands in
+// for missing ones, so that the count per phase stays a power of two, e.g. 7
+// consumer waves of which one adds 2). The caller has already
 // waited for the wave's own LDS writes or reads of the slot; LDS operations
 // of one wave execute in order, so nothing here needs waiting for. The add
 // runs with exec narrowed to lane 0 inside the assembly rather than under a
 // lane test, so the code around it stays wave-uniform and the ring counters
 // stay in scalar registers.
-__device__ __forceinline__ void flag_arrive(uint32_t addr) {
+__device__ __forceinline__ void flag_arrive(uint32_t addr, uint32_t n = 1u) {
     uint64_t saved;
     asm volatile(
         "s_mov_b64 %0, exec\n\t"
@@ -144,7 +146,7 @@ __device__ __forceinline__ void flag_arrive(uint32_t addr) {
         "ds_add_u32 %1, %2\n\t"
         "s_mov_b64 exec, %0"
         : "=&s"(saved)
-        : "v"(addr), "v"(1u)
+        : "v"(addr), "v"(n)
         : "memory");
 }
 
@@ -157,7 +159,7 @@ struct LdsFlags {
     uint32_t fb;            // LDS address of the flag area
     const uint32_t *words;  // the same area as a generic pointer, for early reads
     __device__ void arrive_full(int s) const { flag_arrive(full_flag(fb, s)); }
-    __device__ void arrive_empty(int s) const { flag_arrive(empty_flag(fb, s)); }
+    __device__ void arrive_empty(int s, uint32_t n = 1u) const { flag_arrive(empty_flag(fb, s), n); }
     template <int E>
     __device__ bool wait_full(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {
         return flag_wait<E>(full_flag(fb, s), parity, status, who, t);
