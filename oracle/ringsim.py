@@ -123,6 +123,13 @@ def _is_pow2(x: int) -> bool:
     return x > 0 and (x & (x - 1)) == 0
 
 
+def _pow2_at_least(x: int) -> int:
+    e = 1
+    while e < x:
+        e *= 2
+    return e
+
+
 # ---------------------------------------------------------------------------
 # Exhaustive interleavings
 # ---------------------------------------------------------------------------
@@ -133,7 +140,10 @@ def _is_pow2(x: int) -> bool:
 def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
             max_states: int = 5_000_000, encoding: str = "phase", lookahead: int = 0) -> Result:
     """encoding: "phase" (phase bit + pending count) or "counter" (arrival
-    counter whose bit log2(E) is the phase bit; E must be a power of two).
+    counter whose bit log2(E) is the phase bit). With the counter, a role
+    whose wave count n is not a power of two counts E = the next power of two
+    per phase, and its last wave arrives with weight E - n + 1 (the device's
+    seven attention consumers: six add 1, the seventh 2).
 
     lookahead = 0: each producer fills a buffer and signals it in one go.
     lookahead = D >= 1: asynchronous fills, as on the device: a producer keeps
@@ -147,19 +157,25 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
     one = variant == "one_barrier"
     exp_full = P + C if one else P
     exp_empty = C
+    w_prod = [1] * P  # weight of each wave's arrival (counter encoding)
+    w_cons = [1] * C
     if encoding == "counter":
-        if not (_is_pow2(exp_full) and _is_pow2(exp_empty)):
-            raise ValueError("the counter encoding needs power-of-two arrival counts")
+        if one and not _is_pow2(exp_full):
+            raise ValueError("the single-barrier counter encoding needs a power-of-two arrival count")
+        if not one:
+            w_prod[-1] += _pow2_at_least(P) - P
+        w_cons[-1] += _pow2_at_least(C) - C
+
         # flags are stored as raw counters and viewed through _counter_view
-        def arrive(flag, expected):
-            return flag + 1
+        def arrive(flag, expected, w=1):
+            return flag + w
 
         def view(flag, expected):
-            return _counter_view(flag, expected)
+            return _counter_view(flag, _pow2_at_least(expected))
         init_flag_full = 0
         init_flag_empty = 0
     elif encoding == "phase":
-        def arrive(flag, expected):
+        def arrive(flag, expected, w=1):
             return _arrive(flag, expected)
 
         def view(flag, expected):
@@ -216,7 +232,7 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
             tags[i] = old
             nb[so] = tuple(tags)
             nf = list(fulls)
-            nf[so] = arrive(nf[so], exp_full)
+            nf[so] = arrive(nf[so], exp_full, w_prod[i])
             out.append(with_prod((t, waited, inflight - 1), tuple(nf), tuple(nb)))
             return out
         if t >= T:
@@ -295,7 +311,7 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
                 out.append((tuple(np_), conss, fulls, empties, tuple(nb)))
             else:
                 nf = list(fulls)
-                nf[s] = arrive(nf[s], exp_full)
+                nf[s] = arrive(nf[s], exp_full, w_prod[i])
                 np_ = list(prods)
                 np_[i] = (t + 1, 0)
                 out.append((tuple(np_), conss, tuple(nf), empties, bufs))
@@ -336,7 +352,7 @@ def explore(S: int, T: int, P: int = 1, C: int = 1, variant: str = "standard",
                     out.append((prods, tuple(nc), tuple(nf), empties, bufs))
                 else:
                     ne = list(empties)
-                    ne[s] = arrive(ne[s], exp_empty)
+                    ne[s] = arrive(ne[s], exp_empty, w_cons[j])
                     out.append((prods, tuple(nc), fulls, tuple(ne), bufs))
         return out
 

@@ -145,9 +145,43 @@ def test_counter_encoding_negative_controls(variant):
     assert r.deadlock or r.violation is not None
 
 
-def test_counter_encoding_rejects_non_power_of_two():
+def test_counter_encoding_rejects_non_power_of_two_single_barrier():
     with pytest.raises(ValueError):
-        rs.explore(2, 4, 3, 1, encoding="counter")
+        rs.explore(2, 4, 1, 2, variant="one_barrier", encoding="counter")  # 3 arrivals on one barrier
+
+
+WEIGHTED_CASES = [(S, T, 1, 3) for S in (1, 2, 3) for T in (3, 4)] + [(1, 2, 1, 5), (2, 2, 1, 5), (2, 3, 3, 1),
+                                                                      (2, 2, 3, 3), (1, 2, 1, 7)]
+
+
+@pytest.mark.parametrize("S,T,P,C", WEIGHTED_CASES)
+def test_counter_encoding_weighted_last_wave(S, T, P, C):
+    """A role of n waves, n not a power of two, counts E = next power of two
+    per phase and its last wave adds E - n + 1 (seven attention consumers: the
+    seventh adds 2). Every interleaving stays safe and live, and the reachable
+    producer leads and (producer, consumer) tile pairs are those of the exact
+    count."""
+    a = rs.explore(S, T, P, C)
+    b = rs.explore(S, T, P, C, encoding="counter")
+    assert b.violation is None and not b.deadlock
+    assert (a.max_lead, a.reach_pairs) == (b.max_lead, b.reach_pairs)
+    d = rs.explore(S, T, P, C, lookahead=S, encoding="counter")
+    assert d.violation is None and not d.deadlock
+
+
+def test_counter_view_of_seven_waves():
+    """Six unit arrivals leave the phase open; the seventh wave's double
+    arrival completes it, and the next phase needs all seven again."""
+    view = lambda count: rs._counter_view(count, 8)  # noqa: E731
+    assert [view(c)[0] for c in range(7)] == [0] * 7
+    assert view(6 + 2)[:2] == (1, 8) and view(8)[2] == 1
+    assert view(8 + 6)[0] == 1 and view(8 + 6 + 2)[0] == 0 and view(16)[2] == 2
+
+
+@pytest.mark.parametrize("variant", ["empty_same_parity", "drop_release", "full_parity_flipped"])
+def test_counter_encoding_weighted_negative_controls(variant):
+    r = rs.explore(2, 4, 1, 3, variant=variant, encoding="counter")
+    assert r.deadlock or r.violation is not None
 
 
 LOOKAHEAD_CASES = [(S, T, P, C, D) for S in (1, 2, 3, 4) for T in (4, 7) for P in (1, 2) for C in (1, 2)
