@@ -167,18 +167,21 @@ def test_errors(gpu):
     gpu.check_device_status()
 
 
+@pytest.mark.parametrize("consumers", [7, 4])
 @pytest.mark.parametrize("causal", [False, True])
-def test_full_size_sampled(gpu, causal):
+def test_full_size_sampled(gpu, causal, consumers):
     """The benchmark's shape (batch 4, 32 heads, 4096 x 4096, D 128) in the launch configuration the
-    benchmark times, against the oracle on sampled rows of sampled heads."""
+    benchmark times (one producer, seven consumers) and with four consumers, against the oracle on
+    sampled rows of sampled heads."""
     w = synth.ATTENTION
     Bn, H, S, D = w["batch"], w["heads"], w["S"], w["D"]
     n = Bn * H * S * D
     Q = synth.normal_bf16_bits(synth.seed_for(w["id"], "A"), n, scale=1.0).reshape(Bn, H, S, D)
     K = synth.normal_bf16_bits(synth.seed_for(w["id"], "B"), n, scale=1.0).reshape(Bn, H, S, D)
     V = synth.normal_bf16_bits(synth.seed_for(w["id"], "src"), n, scale=1.0).reshape(Bn, H, S, D)
-    O = run_attention(gpu, Q, K, V, causal, stages=w["stages"], guards=False)
-    rows = np.array([0, 1, 127, 128, 2047, 4000, 4095])
+    O = run_attention(gpu, Q, K, V, causal, stages=w["stages"], guards=False,
+                      config=dict(producer_waves=1, consumer_waves=consumers))
+    rows = np.array([0, 1, 127, 128, 223, 224, 2047, 4000, 4095])
     for b, h in ((0, 0), (3, 31), (2, 17)):
         check(O[b, h, rows], att.attention_rows(Q, K, V, 1.0 / math.sqrt(D), causal, b, h, rows))
     assert np.all(np.isfinite(O))
