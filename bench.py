@@ -15,6 +15,12 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
   roofline             = the GEMM kernel against the fp32 MFMA peak
   copy_roofline        = the copy kernel against the HBM peak
   cpu_baseline         = the CPU oracle on a bounded sample of the same GEMM
+                         (its rows also give `parity`)
+  copy_cpu_baseline    = the copy oracle (a multi-threaded host memcpy of the
+                         same 1 GiB), median of its calls
+  copy.parity          = the timed copy configuration's output against its
+                         source on the GPU and against the oracle's copy on
+                         the host, byte for byte (outside the timed regions)
   homogeneous_baseline = the same GEMM, tile and ring depth on the kernel
                          without roles (every wave loads, barrier, computes)
   vendor_library       = the same GEMM through torch (relu_(addmm), hipBLASLt)
@@ -122,6 +128,33 @@ def time_region(torch, fn, steps: int):
     return wall, sum(per) / len(per), min(per)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_copy(src_host, budget_s: float):
+    """The copy oracle (a multi-threaded host memcpy of the whole buffer) timed call by call
+    until about budget_s; returns (GB/s of the median call, calls, seconds, threads, last output)."""
+    import oracle
+    threads = oracle.host_threads()
+    times, out = [], None
+    while not times or (sum(times) < budget_s and len(times) < 20):
+        t0 = time.perf_counter()
+        out = oracle.copy(src_host, threads=threads)
+        times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
+    return 2.0 * src_host.nbytes / med / 1e9, len(times), sum(times), threads, out
+
+
 def cpu_baseline_gemm(A, B, bias, budget_s: float):
     """The oracle on the first rows of the same GEMM, 16 rows at a time, until
     about budget_s of CPU work; returns (TFLOP/s, rows, seconds, threads, rows_out)."""
@@ -177,7 +210,8 @@ def run(args):
     copy_src = None
     if not args.no_copy:
         nel = cw["bytes"] // 4
-        copy_src = torch.from_numpy(synth.uniform_pm1(synth.seed_for(2, "src"), nel)).to(dev)
+        copy_host = synth.uniform_pm1(synth.seed_for(2, "src"), nel)
+        copy_src = torch.from_numpy(copy_host).to(dev)
         copy_dst = torch.empty_like(copy_src)
         copy_cfg = dict(copy_tile_bytes=args.copy_tile or cw["tile_bytes"], producer_waves=args.copy_producers,
                         copy_workgroups=args.copy_workgroups,
@@ -300,10 +334,14 @@ def run(args):
         result["copy"]["plain_device_copy"] = {"value": round(moved / p_kern / 1e9, 1), "unit": "GB/s",
                                                "kind": "torch Tensor.copy_ on the device"}
         result["copy"]["staged_over_plain"] = round(p_kern / c_kern, 4)
-        copy()  # leave the staged copy's output in dst for --check
-        if args.check:
-            eq = torch.equal(copy_dst, copy_src)
-            result["copy"]["bit_exact_vs_source"] = bool(eq)
+        # parity of the timed launch configuration, outside the timed regions: dst is overwritten
+        # with a sentinel first, so only the staged copy can make it equal to src again
+        copy_dst.fill_(-7.0)
+        copy()
+        torch.cuda.synchronize()
+        result["copy"]["parity"] = {"bytes_checked": nbytes, "kind": "bit-exact, on the GPU",
+                                    "pass": bool(torch.equal(copy_dst.view(torch.int32),
+                                                             copy_src.view(torch.int32)))}
     result["ms_per_step"] = round(step_s * 1e3, 4)
 
     if args.calibrate_copy and copy_src is not None:
@@ -330,11 +368,24 @@ def run(args):
         tf, rows, secs, threads, ref = cpu_baseline_gemm(A, B, bias, args.cpu_budget)
         result["cpu_baseline"] = {"value": round(tf, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                                   "sample": "first %d rows of the %dx%dx%d GEMM (%d x %d x %d), %.1f s"
-                                            % (rows, M, N, K, rows, N, K, secs)}
+                                            % (rows, M, N, K, rows, N, K, secs),
+                                  "cpu_model": cpu_model()}
         got = dC[:rows].cpu().numpy()
         s = oracle.compare(got, ref)
         result["parity"] = {"rows_checked": rows, "max_abs": s["max_abs"], "rel_fro": s["rel_fro"],
                             "pass": bool(oracle.within_tolerance(s, dtype))}
+        if copy_src is not None:
+            log("copy cpu baseline (oracle memcpy of %d bytes)" % nbytes)
+            gbs, calls, csecs, cthreads, host_ref = cpu_baseline_copy(copy_host, args.copy_cpu_budget)
+            result["copy_cpu_baseline"] = {"value": round(gbs, 1), "unit": "GB/s", "cores": cthreads,
+                                           "kind": "oracle",
+                                           "sample": "the whole %d-byte copy, %d calls in %.1f s, median call"
+                                                     % (nbytes, calls, csecs),
+                                           "cpu_model": cpu_model()}
+            # the staged copy's output (left in dst above) against the oracle's, byte for byte
+            mism = oracle.first_mismatch(copy_dst.cpu().numpy(), host_ref)
+            result["copy"]["parity"]["oracle_first_mismatch"] = mism
+            result["copy"]["parity"]["pass"] = result["copy"]["parity"]["pass"] and mism == -1
     return result
 
 
@@ -550,7 +601,8 @@ def main():
                    help="staged copy: ordinary (cached) loads and stores instead of streaming ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    p.add_argument("--check", action="store_true", help="also compare the copy's output on the GPU")
+    p.add_argument("--copy-cpu-budget", type=float, default=5.0,
+                   help="seconds of copy-oracle calls for copy_cpu_baseline")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after timing, run torch's plain 1 GiB device copy 3 times (for counter calibration)")
     p.add_argument("--homogeneous", action="store_true",

@@ -217,6 +217,22 @@ const char *wsg_last_error(void);
 int wsg_check_device_status(void);
 
 /*
+ * Status-word bits, as wsg_check_device_status reads them: WSG_STATUS_TIMEOUT
+ * is set when a wait gave up, together with the bit of the kernel it was in.
+ */
+#define WSG_STATUS_TIMEOUT 1u
+#define WSG_STATUS_COPY 2u
+#define WSG_STATUS_GEMM 4u
+#define WSG_STATUS_ATTENTION 8u
+
+/*
+ * The message wsg_check_device_status reports for a status word `word`
+ * (naming every kernel whose bit is set). Host-only, no device access; the
+ * returned text is thread-local and valid until the thread's next call.
+ */
+const char *wsg_status_message(unsigned word);
+
+/*
  * Wait statistics, a diagnostic of the ring handshake: with wsg_set_wait_stats(1)
  * the calling thread's later launches count, per role, every flag wait, the
  * waits that found the flag not yet flipped, and the polls those took (each

@@ -33,3 +33,22 @@ def gpu():
 def say(msg):
     """Flush a line naming the case before a GPU step."""
     print(msg, flush=True)
+
+
+def stratified_rows(M, tile, seed=0):
+    """Rows to check at full size: three in every `tile`-row block of the output.
+
+    Each output tile row (one workgroup row of the launch) contributes its first
+    row, its last row and one at an offset that moves by 101 rows (mod tile) from
+    one tile row to the next. Over a launch the moving row falls in every
+    consumer wave's row block and at every lane position of a fragment, and
+    every row covers all tile columns, so every workgroup's output tile is
+    compared somewhere.
+    """
+    import numpy as np
+    out = set()
+    for i in range((M + tile - 1) // tile):
+        r0 = i * tile
+        for r in (r0, r0 + tile - 1, r0 + (37 + 101 * i + seed) % tile):
+            out.add(min(M - 1, r))
+    return np.array(sorted(out), dtype=np.int64)

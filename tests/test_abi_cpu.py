@@ -150,3 +150,16 @@ def test_binding_constants_match_header(wsg):
     assert {"WSG_OK", "WSG_EINVAL", "WSG_FP32", "WSG_BF16", "WSG_FLAG_HOMOGENEOUS"} <= set(defs)
     for name, value in defs.items():
         assert getattr(wsg, name) == int(value), name
+
+
+def test_status_message_names_every_kernel(wsg):
+    """Each kernel bit of the status word appears in the timeout message (host-only call)."""
+    T = wsg.WSG_STATUS_TIMEOUT
+    assert "no ring flag wait gave up" in wsg.status_message(0)
+    for bit, name in ((wsg.WSG_STATUS_COPY, "staged_copy"), (wsg.WSG_STATUS_GEMM, "gemm"),
+                      (wsg.WSG_STATUS_ATTENTION, "attention")):
+        msg = wsg.status_message(T | bit)
+        assert name in msg and "gave up" in msg, msg
+    msg = wsg.status_message(T | wsg.WSG_STATUS_COPY | wsg.WSG_STATUS_GEMM | wsg.WSG_STATUS_ATTENTION)
+    assert "staged_copy" in msg and "gemm" in msg and "attention" in msg
+    assert "unnamed" in wsg.status_message(T)

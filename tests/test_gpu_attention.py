@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from conftest import say
+from conftest import say, stratified_rows
 from oracle import attention as att
 
 pytestmark = pytest.mark.gpu
@@ -181,7 +181,9 @@ def test_full_size_sampled(gpu, causal, consumers):
     V = synth.normal_bf16_bits(synth.seed_for(w["id"], "src"), n, scale=1.0).reshape(Bn, H, S, D)
     O = run_attention(gpu, Q, K, V, causal, stages=w["stages"], guards=False,
                       config=dict(producer_waves=1, consumer_waves=consumers))
-    rows = np.array([0, 1, 127, 128, 223, 224, 2047, 4000, 4095])
-    for b, h in ((0, 0), (3, 31), (2, 17)):
-        check(O[b, h, rows], att.attention_rows(Q, K, V, 1.0 / math.sqrt(D), causal, b, h, rows))
+    # every head, three rows of every query tile (each workgroup owns one query tile of one head)
+    for b in range(Bn):
+        for h in range(H):
+            rows = stratified_rows(S, 32 * consumers, b * H + h)
+            check(O[b, h, rows], att.attention_rows(Q, K, V, 1.0 / math.sqrt(D), causal, b, h, rows))
     assert np.all(np.isfinite(O))

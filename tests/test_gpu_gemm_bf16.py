@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from conftest import say
+from conftest import say, stratified_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -136,18 +136,29 @@ def test_power_of_two_scaling_and_determinism(gpu):
 
 
 def test_full_size_workload_sampled(gpu):
-    """8192^3 bf16, N(0,1)*0.1, 4-stage ring, default launch configuration."""
+    """8192^3 bf16, N(0,1)*0.1, 4-stage ring, default launch configuration: three rows of every
+    tile row (every workgroup's output tile) against the oracle, and the reflection C(A, B, b) -
+    C(-A, B, -b) (negating bf16 values flips their sign bit, exactly) against the oracle's
+    pre-activation."""
     w = synth.WORKLOADS[5]
     M, N, K = w["M"], w["N"], w["K"]
     A = synth.normal_bf16_bits(synth.seed_for(5, "A"), M * K).reshape(M, K)
     B = synth.normal_bf16_bits(synth.seed_for(5, "B"), K * N).reshape(K, N)
     bias = synth.normal_bf16_bits(synth.seed_for(5, "bias"), N)
     C = run_gemm(gpu, A, B, bias, stages=w["stages"], guards=False)
-    rng = np.random.default_rng(5)
-    rows = np.array(sorted(set([0, M - 1, M // 2]) | set(rng.integers(0, M, 8).tolist())), dtype=np.int64)
-    assert_close(C[rows], oracle.gemm_bias_relu_rows(A, B, bias, rows))
+    BM = gpu.resolve_config(gpu.WSG_BF16, M, N, K, w["stages"])["BM"]
+    rows = stratified_rows(M, BM, 5)
+    ref = oracle.gemm_bias_relu_rows(A, B, bias, rows)
+    assert_close(C[rows], ref)
     assert np.all(C >= 0) and np.all(np.isfinite(C))
     assert 0.4 < float(np.mean(C == 0)) < 0.6
+    neg = lambda x: x ^ np.uint16(0x8000)  # noqa: E731
+    Cn = run_gemm(gpu, neg(A), B, neg(bias), stages=w["stages"], guards=False)
+    assert not np.any((C > 0) & (Cn > 0)), "a pre-activation and its negation both positive"
+    x_gpu = C[rows].astype(np.float64) - Cn[rows].astype(np.float64)
+    x_ref = ref - oracle.gemm_bias_relu_rows(neg(A), B, neg(bias), rows)
+    s = oracle.compare(x_gpu, x_ref)
+    assert oracle.within_tolerance(s, "bf16"), s
 
 
 def test_argument_errors(gpu):

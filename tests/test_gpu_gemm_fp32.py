@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from conftest import say
+from conftest import say, stratified_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -179,28 +179,37 @@ def test_argument_errors(gpu):
 
 # ---------------------------------------------------------------- full sizes (sampled)
 
-def _sampled_rows(M, count, seed):
-    rng = np.random.default_rng(seed)
-    rows = set([0, M - 1, M // 2]) | set(rng.integers(0, M, count).tolist())
-    return np.array(sorted(rows), dtype=np.int64)
+def _tile_rows(gpu, M, N, K, stages, dtype=None):
+    """BM of the launch configuration the library picks for this problem."""
+    return gpu.resolve_config(gpu.WSG_FP32 if dtype is None else dtype, M, N, K, stages)["BM"]
 
 
 @pytest.mark.parametrize("wid", [3, 4])
 def test_full_size_workload_sampled(gpu, wid):
-    """4096^3 and the ragged 3000x5000x4100 in the default launch configuration."""
+    """4096^3 and the ragged 3000x5000x4100 in the default launch configuration: three rows of
+    every tile row (every workgroup's output tile) against the oracle, and the reflection
+    C(A, B, b) - C(-A, B, -b), which gives back the GPU's own pre-activation (ReLU(x) - ReLU(-x)
+    = x, and negating A and b negates every product and sum exactly), against the oracle's."""
     w = synth.WORKLOADS[wid]
     M, N, K = w["M"], w["N"], w["K"]
     A = synth.uniform_pm1(synth.seed_for(wid, "A"), M * K).reshape(M, K)
     B = synth.uniform_pm1(synth.seed_for(wid, "B"), K * N).reshape(K, N)
     bias = synth.uniform_pm1(synth.seed_for(wid, "bias"), N)
     C = run_gemm(gpu, A, B, bias, stages=w["stages"], guards=False)
-    rows = _sampled_rows(M, 12, wid)
+    rows = stratified_rows(M, _tile_rows(gpu, M, N, K, w["stages"]), wid)
     ref = oracle.gemm_bias_relu_rows(A, B, bias, rows)
     assert_close(C[rows], ref)
     # properties over the whole output
     assert np.all(C >= 0) and np.all(np.isfinite(C))
     frac_zero = float(np.mean(C == 0))
     assert 0.4 < frac_zero < 0.6, frac_zero  # symmetric pre-activations: about half clamp to 0
+    # the negative half: reflected inputs
+    Cn = run_gemm(gpu, -A, B, -bias, stages=w["stages"], guards=False)
+    assert not np.any((C > 0) & (Cn > 0)), "a pre-activation and its negation both positive"
+    x_gpu = C[rows].astype(np.float64) - Cn[rows].astype(np.float64)
+    x_ref = ref - oracle.gemm_bias_relu_rows(-A, B, -bias, rows)
+    s = oracle.compare(x_gpu, x_ref)
+    assert oracle.within_tolerance(s, "fp32"), s
 
 
 @pytest.mark.parametrize("stages", [2, 4])  # 256x128x32 and 256x128x16 tiles
@@ -208,7 +217,7 @@ def test_ragged_full_size_integer_bit_exact(gpu, stages):
     M, N, K = 3000, 5000, 4100
     A, B, bias = int_case(4444, M, N, K)
     C = run_gemm(gpu, A, B, bias, stages=stages, guards=False)
-    rows = _sampled_rows(M, 10, 5)
+    rows = stratified_rows(M, _tile_rows(gpu, M, N, K, stages), 5 + stages)
     assert np.array_equal(C[rows].astype(np.float64), oracle.gemm_bias_relu_rows(A, B, bias, rows))
     # last tile row and column (56 rows, 8 columns past the last full tile)
     cols = np.arange(N - 8, N)

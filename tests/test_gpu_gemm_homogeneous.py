@@ -9,7 +9,8 @@ import synth
 from test_gpu_gemm_bf16 import int_case as int_bf16
 from test_gpu_gemm_bf16 import normal_case
 from test_gpu_gemm_bf16 import run_gemm as run_bf16
-from test_gpu_gemm_fp32 import _sampled_rows, uniform_case
+from conftest import stratified_rows
+from test_gpu_gemm_fp32 import uniform_case
 from test_gpu_gemm_fp32 import int_case as int_f32
 from test_gpu_gemm_fp32 import run_gemm as run_f32
 
@@ -118,7 +119,7 @@ def test_full_size_fp32_sampled(gpu):
     B = synth.uniform_pm1(synth.seed_for(3, "B"), K * N).reshape(K, N)
     bias = synth.uniform_pm1(synth.seed_for(3, "bias"), N)
     C = run_f32(gpu, A, B, bias, stages=2, config=dict(flags=HOMOGENEOUS), guards=False)
-    rows = _sampled_rows(M, 8, 33)
+    rows = stratified_rows(M, 256, 33)
     s = oracle.compare(C[rows], oracle.gemm_bias_relu_rows(A, B, bias, rows))
     assert oracle.within_tolerance(s, "fp32"), s
     assert np.all(C >= 0) and np.all(np.isfinite(C))
@@ -128,7 +129,7 @@ def test_ragged_full_size_integer_bit_exact(gpu):
     M, N, K = 3000, 5000, 4100
     A, B, bias = int_f32(4545, M, N, K)
     C = run_f32(gpu, A, B, bias, stages=2, config=dict(flags=HOMOGENEOUS), guards=False)
-    rows = _sampled_rows(M, 6, 7)
+    rows = stratified_rows(M, 256, 7)
     assert np.array_equal(C[rows].astype(np.float64), oracle.gemm_bias_relu_rows(A, B, bias, rows))
     cols = np.arange(N - 8, N)
     ms = np.repeat(np.arange(M - 56, M), cols.size)

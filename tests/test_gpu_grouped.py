@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from conftest import say
+from conftest import say, stratified_rows
 from test_gpu_gemm_fp32 import run_gemm as run_f32
 
 pytestmark = pytest.mark.gpu
@@ -212,9 +212,10 @@ def test_full_size_moe_layer_sampled(gpu):
     B = synth.normal_bf16_bits(synth.seed_for(w["id"], "B"), G * K * N).reshape(G, K, N)
     bias = synth.normal_bf16_bits(synth.seed_for(w["id"], "bias"), G * N).reshape(G, N)
     C = run_grouped(gpu, A, B, bias, rows, stages=w["stages"], guards=False)
+    # three rows of every tile row of every expert (each expert's tiles start at its first row)
+    BM = gpu.resolve_config(gpu.WSG_BF16, M, N, K, w["stages"])["BM"]
     starts = np.concatenate([[0], np.cumsum(rows)])
-    want = np.concatenate([[starts[e], starts[e] + rows[e] - 1, (starts[e] + starts[e + 1]) // 2]
-                           for e in range(G) if rows[e]])
+    want = np.concatenate([starts[e] + stratified_rows(rows[e], BM, e) for e in range(G) if rows[e]])
     s = oracle.compare(C[want], oracle.grouped_gemm_bias_relu_rows(A, B, bias, rows, want))
     assert oracle.within_tolerance(s, "bf16"), s
     assert np.all(C >= 0) and np.all(np.isfinite(C))

@@ -52,3 +52,27 @@ def test_copy_wait_counts_match_protocol(gpu):
     assert torch.equal(dst, src)
     assert st["copy_consumer_full"]["waits"] == ntiles * 2
     assert st["copy_producer_empty"]["waits"] == ntiles * 2
+
+
+@pytest.mark.parametrize("D,consumers", [(64, 4), (128, 7)])
+def test_attention_wait_counts_match_protocol(gpu, D, consumers):
+    """Attention consumers wait once per key tile (64 keys) each; the binding reports their counters."""
+    import torch
+    Bn, H, Sq, Skv = 1, 2, 300, 200
+    dev = lambda seed, s: torch.from_numpy(synth.normal_bf16_bits(seed, int(np.prod(s)), scale=1.0)  # noqa: E731
+                                           .reshape(s).view(np.int16)).cuda()
+    q, k, v = dev(31, (Bn, H, Sq, D)), dev(32, (Bn, H, Skv, D)), dev(33, (Bn, H, Skv, D))
+    gpu.read_wait_stats()
+    gpu.set_wait_stats(True)
+    try:
+        say("attention wait stats D=%d consumers=%d" % (D, consumers))
+        gpu.attention_fwd(q, k, v, stages=2, config=dict(producer_waves=1, consumer_waves=consumers))
+        st = gpu.read_wait_stats()
+    finally:
+        gpu.set_wait_stats(False)
+    q_tiles = -(-Sq // (32 * consumers))
+    key_tiles = -(-Skv // 64)
+    a = st["attention_consumer_full"]
+    assert a["waits"] == Bn * H * q_tiles * consumers * key_tiles, a
+    assert a["blocked"] <= a["waits"]
+    assert st["gemm_consumer_full"]["waits"] == 0 and st["copy_consumer_full"]["waits"] == 0

@@ -21,7 +21,7 @@ __all__ = [
     "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "attention_fwd",
     "resolve_config",
     "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
-    "set_stream", "get_stream",
+    "set_stream", "get_stream", "status_message",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
     "WSG_FLAG_HOMOGENEOUS", "WSG_MAX_GROUPS",
 ]
@@ -40,12 +40,16 @@ WSG_FLAG_GENERAL_PRODUCER = 1
 WSG_FLAG_NONTEMPORAL = 2
 WSG_FLAG_HOMOGENEOUS = 4
 WSG_MAX_GROUPS = 64
+WSG_STATUS_TIMEOUT = 1
+WSG_STATUS_COPY = 2
+WSG_STATUS_GEMM = 4
+WSG_STATUS_ATTENTION = 8
 
 # every function include/wsg.h declares
 EXPORTS = (
     "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "attention_fwd",
     "wsg_gemm_resolve_config", "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
-    "wsg_check_device_status", "wsg_set_wait_stats", "wsg_read_wait_stats", "wsg_version",
+    "wsg_check_device_status", "wsg_status_message", "wsg_set_wait_stats", "wsg_read_wait_stats", "wsg_version",
 )
 
 
@@ -90,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "wsg_get_stream": ([], vp),
         "wsg_last_error": ([], ctypes.c_char_p),
         "wsg_check_device_status": ([], ci),
+        "wsg_status_message": ([ctypes.c_uint], ctypes.c_char_p),
         "wsg_set_wait_stats": ([ci], ci),
         "wsg_read_wait_stats": ([ctypes.POINTER(ctypes.c_uint64)], ci),
         "wsg_version": ([], ctypes.c_char_p),
@@ -318,8 +323,14 @@ def read_wait_stats() -> dict:
     buf = (ctypes.c_uint64 * 16)()
     _raise_on(lib.wsg_read_wait_stats(buf))
     v = list(buf)
-    names = ("gemm_consumer_full", "gemm_producer_empty", "copy_consumer_full", "copy_producer_empty")
+    names = ("gemm_consumer_full", "gemm_producer_empty", "copy_consumer_full", "copy_producer_empty",
+             "attention_consumer_full")
     return {n: {"waits": v[3 * i], "blocked": v[3 * i + 1], "polls": v[3 * i + 2]} for i, n in enumerate(names)}
+
+
+def status_message(word: int) -> str:
+    """The text check_device_status reports for a device status word (host only)."""
+    return lib.wsg_status_message(int(word) & 0xFFFFFFFF).decode()
 
 
 def check_device_status() -> None:

@@ -16,6 +16,10 @@ __device__ unsigned wsg_status_word;
 // Wait statistics (see wsg_read_wait_stats); each GPU holds its own copy.
 __device__ unsigned long long wsg_wait_stats[wsg::kStatWords];
 
+static_assert(wsg::kStatusTimeout == WSG_STATUS_TIMEOUT && wsg::kStatusCopy == WSG_STATUS_COPY &&
+                  wsg::kStatusGemm == WSG_STATUS_GEMM && wsg::kStatusAttention == WSG_STATUS_ATTENTION,
+              "status bits of the kernels and of the public header");
+
 namespace {
 
 thread_local hipStream_t tl_stream = nullptr;
@@ -212,6 +216,20 @@ int copy_impl(const void *src, void *dst, size_t bytes, int stages, const wsg_co
 
 namespace wsg {
 
+std::string timeout_message(unsigned word) {
+    if (!(word & kStatusTimeout)) return "no ring flag wait gave up";
+    std::string who;
+    const std::pair<unsigned, const char *> kernels[] = {
+        {kStatusCopy, "staged_copy"}, {kStatusGemm, "gemm"}, {kStatusAttention, "attention"}};
+    for (const auto &k : kernels) {
+        if (!(word & k.first)) continue;
+        if (!who.empty()) who += " and ";
+        who += k.second;
+    }
+    if (who.empty()) who = "an unnamed kernel";
+    return "a ring flag wait gave up in " + who + " (protocol fault)";
+}
+
 int prepare_kernel(const void *kernel, const DeviceInfo &dev, std::string *err) {
     std::lock_guard<std::mutex> lock(g_kernel_mu);
     bool &done = g_prepared[{dev.device, kernel}];
@@ -319,12 +337,14 @@ int wsg_check_device_status(void) {
     e = hipMemcpy(&word, dev.status, sizeof word, hipMemcpyDeviceToHost);
     if (e == hipSuccess) e = hipMemcpy(dev.status, &zero, sizeof zero, hipMemcpyHostToDevice);
     if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("status word copy: ") + hipGetErrorString(e));
-    if (word & wsg::kStatusTimeout) {
-        std::string who = (word & wsg::kStatusCopy) ? "staged_copy" : "";
-        if (word & wsg::kStatusGemm) who += who.empty() ? "gemm" : " and gemm";
-        return fail(WSG_ETIMEOUT, "a ring flag wait gave up in " + who + " (protocol fault)");
-    }
+    if (word & wsg::kStatusTimeout) return fail(WSG_ETIMEOUT, wsg::timeout_message(word));
     return ok();
+}
+
+const char *wsg_status_message(unsigned word) {
+    thread_local std::string msg;
+    msg = wsg::timeout_message(word);
+    return msg.c_str();
 }
 
 int wsg_set_wait_stats(int enable) {

@@ -52,6 +52,9 @@ struct CopyPlan {
     size_t lds_bytes = 0;
 };
 
+// The text wsg_check_device_status reports for a status word.
+std::string timeout_message(unsigned word);
+
 // Once per (device, kernel): raise the kernel's dynamic-LDS limit to the
 // device maximum, so that launches need no attribute call of their own.
 int prepare_kernel(const void *kernel, const DeviceInfo &dev, std::string *err);

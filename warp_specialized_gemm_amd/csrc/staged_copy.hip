@@ -56,9 +56,16 @@ __global__ void __launch_bounds__((P + C) * 64)
             const int s = (int)(j % S);
             const uint64_t base = (g + (uint64_t)j * G) * (uint64_t)TILE;
             const uint64_t valid = min((uint64_t)TILE, bytes - base);
-            if ((valid & 15u) && wave == 0) {
+            const uint64_t v16 = valid & ~(uint64_t)15;
+            // The partial 16-byte chunk at v16 lies past the buffer range, so
+            // an LDS-DMA load of this tile has already written zeros over it:
+            // the one issued by the wave that owns v16's 1 KiB block, (v16 /
+            // 1024) mod P. That wave alone writes the tail bytes, after the
+            // vmcnt wait that completed its own loads of the tile, so its
+            // ds_write lands after those zeros (one wave's LDS writes are
+            // ordered). Another wave could not know when the zeros land.
+            if ((valid & 15u) && wave == (int)((v16 >> 10) % (uint64_t)P)) {
                 // bytes past the last whole 16-byte chunk: byte loads into the slot
-                const uint64_t v16 = valid & ~(uint64_t)15;
                 if ((uint64_t)lane < (valid - v16)) {
                     unsigned char b = src[base + v16 + lane];
                     ring[(size_t)s * TILE + v16 + lane] = b;
