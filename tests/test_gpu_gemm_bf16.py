@@ -106,6 +106,9 @@ VARIANTS = [
     # 48-deep k tiles: rows of 6 chunks, rotation swizzle; K = 296 leaves an 8-deep last tile
     dict(BM=256, BN=128, BK=48, producer_waves=4, consumer_waves=4, group_k=16),
     dict(BM=256, BN=128, BK=48, producer_waves=2, consumer_waves=4, group_k=16),
+    # 256x256 tiles: 4 producers + 8 consumers (three waves per SIMD), single-fragment consumer walk
+    dict(BM=256, BN=256, BK=32, producer_waves=4, consumer_waves=8),
+    dict(BM=256, BN=256, BK=64, producer_waves=4, consumer_waves=8),
 ]
 
 

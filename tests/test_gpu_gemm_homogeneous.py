@@ -23,7 +23,8 @@ F32_TILES = [dict(BM=256, BN=128, BK=32, consumer_waves=4), dict(BM=256, BN=128,
              dict(BM=128, BN=128, BK=32, consumer_waves=4), dict(BM=64, BN=64, BK=16, consumer_waves=4)]
 BF16_TILES = [dict(BM=256, BN=128, BK=64, consumer_waves=4), dict(BM=256, BN=128, BK=64, consumer_waves=8),
               dict(BM=256, BN=128, BK=32, consumer_waves=4), dict(BM=128, BN=128, BK=32, consumer_waves=4),
-              dict(BM=64, BN=64, BK=32, consumer_waves=4), dict(BM=256, BN=128, BK=48, consumer_waves=4)]
+              dict(BM=64, BN=64, BK=32, consumer_waves=4), dict(BM=256, BN=128, BK=48, consumer_waves=4),
+              dict(BM=256, BN=256, BK=32, consumer_waves=8)]
 
 
 def _h(cfg):
@@ -109,6 +110,14 @@ def test_same_bits_as_the_specialized_kernel(gpu):
     Cb_h = run_bf16(gpu, Ab, Bb, bb, stages=2, config=_h(dict(BM=256, BN=128, BK=64, consumer_waves=4)),
                     guards=False)
     assert np.array_equal(Cb_h.view(np.uint32), Cb_spec.view(np.uint32))
+    # 256 x 256 tiles: the single-fragment consumer walk of the specialized kernel (three waves per SIMD)
+    # and the homogeneous kernel's group-at-a-time MFMAs accumulate every block in the same k order
+    for bk, stages in ((32, 4), (32, 2)):
+        Cw_spec = run_bf16(gpu, Ab, Bb, bb, stages=stages, config=dict(BM=256, BN=256, BK=bk, producer_waves=4,
+                                                                       consumer_waves=8), guards=False)
+        Cw_h = run_bf16(gpu, Ab, Bb, bb, stages=stages, config=_h(dict(BM=256, BN=256, BK=bk, consumer_waves=8)),
+                        guards=False)
+        assert np.array_equal(Cw_h.view(np.uint32), Cw_spec.view(np.uint32)), (bk, stages)
 
 
 def test_full_size_fp32_sampled(gpu):

@@ -495,6 +495,92 @@ __device__ __forceinline__ bool consume_tiles(int T, int S, unsigned char *ring,
 }
 
 // ----------------------------------------------------------------------------
+// Consumer walk for workgroups of more than 8 waves (three waves share a SIMD,
+// so each has at most 168 registers: a 128 x 64 bf16 wave tile's 128
+// accumulators leave room for one set of fragments, not two). The wave keeps
+// ONE fragment set. `step(next_slot, next_k, mid)` runs the current k step's
+// MFMAs and re-reads each fragment piece for the next k step as soon as the
+// last MFMA of this step that uses it has issued, so the next step's LDS
+// reads still fly under this step's MFMAs; the second consumer on the SIMD
+// covers what remains. `mid()` runs after the step's first column block of
+// MFMAs has issued and before its first re-read. KS k steps of 16 per tile
+// (KS >= 2). Flags only at tile boundaries: the next tile's full flag is read
+// early with the reads of the tile's last step. In the last step, `mid`
+// waits for every read of the slot (the last of them fed the MFMAs just
+// issued, so nothing is left to wait for in the steady state), releases the
+// slot and waits for the next tile's full flag; the step's re-reads then come
+// from the next slot (after the last tile: a slot no producer writes any
+// more, values unused).
+// Returns false if a wait gave up.
+// ----------------------------------------------------------------------------
+template <int KS, int P, int C, typename Flags, typename Prime, typename Step>
+__device__ __forceinline__ bool consume_lean(int T, int S, unsigned char *ring, int slot_bytes, const Flags &fl,
+                                             unsigned *status, WaitTally &tally, Prime prime, Step step) {
+    static_assert(KS >= 2, "the lean walk reads the next tile's flag one k step early");
+    if (T == 0) return true;
+    if (!fl.template wait_full<P>(0, 0u, status, kStatusGemm, tally)) return false;
+    prime(ring, 0);
+    // Nothing in flight when the loop starts (the kernel's scalar loads share
+    // the LDS counter and return out of order): without this the compiler
+    // drains the counter at the top of every step instead of waiting only for
+    // the fragments the step's first MFMAs use.
+    wait_lgkm0();
+    // One k step per iteration: each fragment piece re-read in the body is the
+    // loop-carried value of the piece it replaces, so the register allocator
+    // gives both the same registers (unrolled steps rotated through half as
+    // many again and spilled accumulators).
+    uint32_t peek = 0;  // the next tile's full flag as read one step earlier
+    int cs = 0, ks = 0;
+    uint32_t lap = 0;
+    const int U = T * KS;
+    bool ok = true;
+    for (int u = 0; u < U; ++u) {
+        const bool last = ks == KS - 1;
+        const int ns = cs + 1 == S ? 0 : cs + 1;
+        const uint32_t nlap = ns == 0 ? lap + 1 : lap;
+        ok = step(ring + (size_t)(last ? ns : cs) * slot_bytes, last ? 0 : ks + 1, [&]() -> bool {
+            if (last) {
+                wait_lgkm0();  // every read of this tile (and the early flag value) has landed
+                // Two consumers share each SIMD's matrix unit, which issues
+                // the older wave's MFMAs first, so one consumer drifted up to
+                // a tile ahead of its sibling and the slot the laggard still
+                // held took the producers' lead (traced on MI355X: the 8
+                // consumers released a tile 2500-3800 cycles apart). The
+                // consumers that release a slot in the later half raise their
+                // wave priority for the next tile, the earlier half lower it.
+                if (fl.template arrive_empty_rank<C>(cs) >= (uint32_t)(C / 2))
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(0);
+                if (u + 1 < U) {
+                    if (phase_of<P>(__builtin_amdgcn_readfirstlane(peek)) == (nlap & 1u)) {
+                        if (!fl.template wait_full<P, false>(ns, nlap & 1u, status, kStatusGemm, tally))
+                            return false;
+                    } else {
+                        ++tally.waits;  // satisfied by the early read
+                    }
+                }
+                asm volatile("" ::: "memory");
+            }
+            // the next tile's full flag, for the tile's last step (read in
+            // every step; in the last step it is overwritten before use)
+            peek = fl.peek_full(ns);
+            return true;
+        });
+        if (!ok) break;
+        if (last) {
+            cs = ns;
+            lap = nlap;
+            ks = 0;
+        } else {
+            ++ks;
+        }
+    }
+    if (!ok) atomicOr(status, kStatusTimeout | kStatusGemm);  // the wait in the loop gave up
+    return ok;
+}
+
+// ----------------------------------------------------------------------------
 // Homogeneous K loop, the baseline that specialization is measured against
 // (pwwt.cn article, section 1.1: every thread loads the next tile into shared
 // memory, a block barrier, every thread computes, a second barrier before the
@@ -798,9 +884,73 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
             }
     };
 
+    // More than 8 waves: three share a SIMD (168 registers each), so the
+    // consumers keep a single fragment set (consume_lean).
+    constexpr bool LEAN = P > 0 && P + NCW > 8;
     if constexpr (P == 0) {
         static_assert(DMA, "the homogeneous loop loads by LDS-DMA");
         sync_loop<BM, BN, BK, 2, NCW, KG, Frag>(a, ring, cw, lane, m0, n0, T, read, mma);
+    } else if constexpr (LEAN) {
+        constexpr int KS = BK / 16;
+        struct LeanFrag {
+            bf16x8 a[FM];
+            v4i16 lo[FN], hi[FN];
+        };
+        LeanFrag lf;
+        // One lane register per operand. A: row blocks 32 rows apart share the
+        // row swizzle for 4 or 8 chunks per row (it depends on the row mod 16),
+        // 2 * step + h = (2 * step) ^ h, and a row's start is a multiple of its
+        // QPR * 16 bytes while the chunk offset is below that, so
+        // address = slot + 32 i QPR 16 + (a_lane ^ 32 step). B: column blocks
+        // 32 apart move the chunk index by 4 j, a bit the within-wave column
+        // bits never set, so b_col[j] = b_col[0] ^ 64 j; the row offset is a
+        // multiple of the row's BN * 2 bytes, above every column offset.
+        static_assert(QPR == 4 || QPR == 8, "lean walk: k tiles of 32 or 64");
+        const uint32_t a_lane = (uint32_t)a_off[0] | (uint32_t)((h ^ a_swz[0]) << 4);
+        const uint32_t b_lane = (uint32_t)b_row | (uint32_t)b_col[0];
+        auto rd_a = [&](int i, const unsigned char *slot, int step) {
+            lf.a[i] = *reinterpret_cast<const bf16x8 *>(slot + i * 32 * QPR * 16 + (a_lane ^ (uint32_t)(32 * step)));
+        };
+        auto rd_b = [&](int j, const unsigned char *slot, int step) {
+            const unsigned char *p = slot + A_BYTES + 16 * step * BN * 2 + (b_lane ^ (uint32_t)(64 * j));
+            lf.lo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+            lf.hi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 4 * BN * 2));
+        };
+        auto prime = [&](const unsigned char *slot, int step) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) rd_b(j, slot, step);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) rd_a(i, slot, step);
+        };
+        // One k step: column block j's MFMAs over every row block i; B[j] is
+        // re-read once its FM MFMAs have issued, and in the last column block
+        // each A[i] right after its MFMA. The order is pinned (no instruction
+        // crosses a sched_barrier(0)), so every re-read follows the last use
+        // of the registers it overwrites and the two never need to coexist.
+        auto step = [&](const unsigned char *nslot, int nstep, auto mid) -> bool {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const bf16x8 b =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lf.lo[j], lf.hi[j], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf.a[i], b, acc[i][j], 0, 0, 0);
+                    if (j == FN - 1) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        rd_a(i, nslot, nstep);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (j == 0 && !mid()) return false;
+                rd_b(j, nslot, nstep);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return true;
+        };
+        WaitTally tally;
+        if (!consume_lean<KS, P, NCW>(T, S, ring, SLOT, fl, a.status, tally, prime, step)) return;
+        publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
     } else {
         WaitTally tally;
         if (!consume_tiles<KG, P, Frag, GS * FM * FN>(T, S, ring, SLOT, fl, a.status, tally, read, mma)) return;
@@ -816,6 +966,34 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
     float bv[FN];  // all bias loads before the first store, as in the fp32 epilogue
 #pragma unroll
     for (int j = 0; j < FN; ++j) bv[j] = cbase + 32 * j < cols_valid ? bf16_to_f32(bias[cbase + 32 * j]) : 0.0f;
+    if constexpr (LEAN) {
+        // Buffer stores through a resource at the tile's origin: each lane
+        // keeps one 32-bit offset (its row and column) and adds the store's
+        // row and column block (a scalar) into a temporary per store. The
+        // resource's range ends after the last valid element, so rows past M
+        // are dropped by the range check, which covers the VGPR offset (the
+        // scalar-offset operand stays 0); columns past N (which would land in
+        // the next row) are masked per lane. 64-bit addresses per store took
+        // registers the 128 accumulators do not leave. The planner picks
+        // these kernels only when BM rows of C span less than 2^31 bytes.
+        const uint32_t nbytes = (uint32_t)(((int64_t)(rows_valid - 1) * N + cols_valid) * 4);
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(ctile, nbytes);
+        const uint32_t voff = (uint32_t)(rbase * (int)N + cbase) * 4u;
+        const uint32_t row4 = (uint32_t)N * 4u;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if (cbase + 32 * j >= cols_valid) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t soff = (uint32_t)(32 * i + 8 * (r >> 2) + (r & 3)) * row4 + 128u * j;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(relu_f32(acc[i][j][r] + bv[j])), rc,
+                                                          voff + soff, 0, 0);
+                }
+        }
+        return;
+    }
     if (rows_valid == BM && cols_valid == BN) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -892,9 +1070,13 @@ const GemmVariant kGemmVariants[] = {
     WSG_BF(128, 128, 64, 1, 2, 2, true, 32),  WSG_BF(128, 128, 32, 1, 2, 2, true, 16),
     WSG_BF(64, 64, 32, 1, 2, 2, true, 16),    WSG_BF(256, 128, 32, 1, 2, 2, false, 32),
     WSG_BF(128, 128, 32, 1, 2, 2, false, 16), WSG_BF(64, 64, 32, 1, 2, 2, false, 16),
+    // bf16, 256 x 256 tiles: 8 consumer waves of 128 x 64 and 4 producers,
+    // three waves per SIMD, consumers on the single-fragment walk
+    WSG_BF(256, 256, 64, 4, 2, 4, true, 16),  WSG_BF(256, 256, 32, 4, 2, 4, true, 16),
     // bf16, homogeneous
     WSG_BF(256, 128, 64, 0, 2, 2, true, 32),  WSG_BF(256, 128, 64, 0, 4, 2, true, 32),
     WSG_BF(256, 128, 48, 0, 2, 2, true, 16),
+    WSG_BF(256, 256, 32, 0, 2, 4, true, 16),
     WSG_BF(256, 128, 32, 0, 2, 2, true, 32),  WSG_BF(128, 128, 32, 0, 2, 2, true, 16),
     WSG_BF(64, 64, 32, 0, 2, 2, true, 16),
 };
@@ -923,7 +1105,8 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
                "WSG_FLAG_GENERAL_PRODUCER clear";
         return WSG_EINVAL;
     }
-    if (!BM && !BN && !BK) {
+    const bool default_tile = !BM && !BN && !BK;
+    if (default_tile) {
         // default tile by problem size: small problems need more workgroups
         const int64_t big = (M + 255) / 256 * ((N + 127) / 128);
         const int64_t mid = (M + 127) / 128 * ((N + 127) / 128);
@@ -947,25 +1130,42 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
                " and A and B 16-byte aligned";
         return WSG_EUNSUPPORTED;
     }
-    const GemmVariant *pick = nullptr;
     bool lds_short = false;
-    for (int pass = 0; pass < 2 && !pick; ++pass) {
-        const bool want_dma = pass == 0;
-        if (want_dma && (force_general || !aligned)) continue;
-        for (const GemmVariant &v : kGemmVariants) {
-            if (v.dtype != dtype || v.dma != want_dma || (v.P == 0) != homogeneous) continue;
-            if ((BM && v.BM != BM) || (BN && v.BN != BN) || (BK && v.BK != BK)) continue;
-            if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW) || (GK && v.GK != GK)) continue;
-            if (want_dma && ((int64_t)v.BM * K * esz >= 0x7FFFFFFF || (int64_t)v.BK * N * esz >= 0x7FFFFFFF))
-                continue;
-            const size_t need = (size_t)kFlagBytes + (size_t)stages * (size_t)(v.BM * v.BK + v.BK * v.BN) * esz;
-            if (need > dev.max_lds) {
-                lds_short = true;  // a smaller BK of the same tile may still fit
-                continue;
+    auto search = [&](int qBM, int qBN) -> const GemmVariant * {
+        for (int pass = 0; pass < 2; ++pass) {
+            const bool want_dma = pass == 0;
+            if (want_dma && (force_general || !aligned)) continue;
+            for (const GemmVariant &v : kGemmVariants) {
+                if (v.dtype != dtype || v.dma != want_dma || (v.P == 0) != homogeneous) continue;
+                if ((qBM && v.BM != qBM) || (qBN && v.BN != qBN) || (BK && v.BK != BK)) continue;
+                if ((P && v.P != P) || (CW && v.CWM * v.CWN != CW) || (GK && v.GK != GK)) continue;
+                if (want_dma && ((int64_t)v.BM * K * esz >= 0x7FFFFFFF || (int64_t)v.BK * N * esz >= 0x7FFFFFFF))
+                    continue;
+                // more than 8 waves: the buffer-store epilogue addresses BM rows of C with 32-bit offsets
+                if (v.P + v.CWM * v.CWN > 8 && (int64_t)v.BM * N * 4 >= 0x7FFFFFFF) continue;
+                const size_t need = (size_t)kFlagBytes + (size_t)stages * (size_t)(v.BM * v.BK + v.BK * v.BN) * esz;
+                if (need > dev.max_lds) {
+                    lds_short = true;  // a smaller BK of the same tile may still fit
+                    continue;
+                }
+                return &v;
             }
-            pick = &v;
-            break;
         }
+        return nullptr;
+    };
+    // bf16 defaults on large problems: 256 x 256 tiles (8 consumer and 4
+    // producer waves) where their ring fits, 64 deep for up to 2 stages and
+    // 32 deep for 4; at 3 stages the 256 x 128 x 64 tile is faster (measured
+    // on MI355X, 8192^3 in one interleaved run: 256 x 256 x 32 at S = 4 1016
+    // TFLOP/s against 910 for 256 x 128 x 48; at S = 3, 1023 against 1073
+    // for 256 x 128 x 64; at S = 2, 1102 for 256 x 256 x 64).
+    const GemmVariant *pick = nullptr;
+    if (default_tile && dtype == WSG_BF16 && !homogeneous && !P && !CW && !GK && stages != 3 && BM == 256 &&
+        (M + 255) / 256 * ((N + 255) / 256) >= (int64_t)dev.cu_count)
+        pick = search(256, 256);
+    if (!pick) {
+        lds_short = false;
+        pick = search(BM, BN);
     }
     if (!pick && lds_short) {
         *err = "no built " + std::to_string(BM) + "x" + std::to_string(BN) + " tile fits a " + std::to_string(stages) +

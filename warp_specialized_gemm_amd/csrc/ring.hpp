@@ -95,7 +95,9 @@ struct WaitTally {
 // that parity has completed. Returns false (after recording the timeout)
 // when the wait gives up.
 // `poll` returns the flag word (wave-uniform).
-template <int E, typename Poll>
+// RECORD = false leaves the status word to the caller, which records the
+// timeout once outside its loop (so the loop keeps no registers for it).
+template <int E, bool RECORD = true, typename Poll>
 __device__ __forceinline__ bool flag_wait_with(Poll poll, uint32_t parity, unsigned *status, unsigned who,
                                                WaitTally &tally) {
     uint32_t spins = 0;
@@ -109,17 +111,17 @@ __device__ __forceinline__ bool flag_wait_with(Poll poll, uint32_t parity, unsig
         }
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
-            atomicOr(status, kStatusTimeout | who);  // every lane: keeps the loop wave-uniform
+            if constexpr (RECORD) atomicOr(status, kStatusTimeout | who);  // every lane: keeps the loop uniform
             return false;
         }
     }
 }
 
-template <int E>
+template <int E, bool RECORD = true>
 __device__ __forceinline__ bool flag_wait(uint32_t addr, uint32_t parity, unsigned *status, unsigned who,
                                           WaitTally &tally) {
-    return flag_wait_with<E>([&] { return __builtin_amdgcn_readfirstlane(flag_load(addr)); }, parity, status, who,
-                             tally);
+    return flag_wait_with<E, RECORD>([&] { return __builtin_amdgcn_readfirstlane(flag_load(addr)); }, parity, status,
+                                     who, tally);
 }
 
 // Add a wave's tally to stats[0..2] (once per wave, at its end).
@@ -150,6 +152,46 @@ __device__ __forceinline__ void flag_arrive(uint32_t addr, uint32_t n = 1u) {
         : "memory");
 }
 
+// The same arrival of N (an immediate) on a flag whose LDS address is
+// wave-uniform (an SGPR): address and count are moved into VGPRs inside the
+// assembly, so no register holds them between arrivals.
+template <uint32_t N = 1u>
+__device__ __forceinline__ void flag_arrive_uniform(uint32_t addr) {
+    uint64_t saved;
+    uint32_t va, vn;
+    asm volatile(
+        "s_mov_b64 %0, exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "v_mov_b32 %1, %3\n\t"
+        "v_mov_b32 %2, %4\n\t"
+        "ds_add_u32 %1, %2\n\t"
+        "s_mov_b64 exec, %0"
+        : "=&s"(saved), "=&v"(va), "=&v"(vn)
+        : "s"(addr), "n"(N)
+        : "memory");
+}
+
+// One arrival on a flag with E expected arrivals per phase (wave-uniform LDS
+// address), returning how many arrivals of the current phase preceded it
+// (0 .. E - 1). The add returns a value, so its wait is inside the assembly.
+template <int E>
+__device__ __forceinline__ uint32_t flag_arrive_rank(uint32_t addr) {
+    uint64_t saved;
+    uint32_t va, vn, old;
+    asm volatile(
+        "s_mov_b64 %0, exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "v_mov_b32 %1, %4\n\t"
+        "v_mov_b32 %2, 1\n\t"
+        "ds_add_rtn_u32 %3, %1, %2\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b64 exec, %0"
+        : "=&s"(saved), "=&v"(va), "=&v"(vn), "=&v"(old)
+        : "s"(addr)
+        : "memory");
+    return __builtin_amdgcn_readfirstlane(old) & (uint32_t)(E - 1);
+}
+
 // ---------------------------------------------------------------------------
 // The ring's flag words as the kernels use them: full[s] and empty[s] in the
 // first kFlagBytes of the workgroup's LDS, one ds_* instruction per flag
@@ -160,13 +202,20 @@ struct LdsFlags {
     const uint32_t *words;  // the same area as a generic pointer, for early reads
     __device__ void arrive_full(int s) const { flag_arrive(full_flag(fb, s)); }
     __device__ void arrive_empty(int s, uint32_t n = 1u) const { flag_arrive(empty_flag(fb, s), n); }
-    template <int E>
+    template <int E, bool RECORD = true>
     __device__ bool wait_full(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {
-        return flag_wait<E>(full_flag(fb, s), parity, status, who, t);
+        return flag_wait<E, RECORD>(full_flag(fb, s), parity, status, who, t);
+    }
+    __device__ void arrive_empty_uniform(int s) const {
+        flag_arrive_uniform(__builtin_amdgcn_readfirstlane(empty_flag(fb, s)));
     }
     template <int E>
+    __device__ uint32_t arrive_empty_rank(int s) const {
+        return flag_arrive_rank<E>(__builtin_amdgcn_readfirstlane(empty_flag(fb, s)));
+    }
+    template <int E, bool RECORD = true>
     __device__ bool wait_empty(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {
-        return flag_wait<E>(empty_flag(fb, s), parity, status, who, t);
+        return flag_wait<E, RECORD>(empty_flag(fb, s), parity, status, who, t);
     }
     // early read of full[s] by a consumer (which has no LDS-DMA in flight);
     // the compiler waits for it where the value is used

@@ -36,15 +36,18 @@ __device__ __forceinline__ LdsFlags init_flags(unsigned char *lds) {
 
 // XOR applied to the chunk index of row m (QPR chunks of 16 bytes per row),
 // chosen so that the 16 consecutive rows one 16-lane read pass covers land on
-// 16 distinct 16-byte positions of a 256-byte bank span. 8 chunks (128-byte
-// rows): (m / 2) mod 8, each parity class of 8 rows covering all 8 chunks;
-// 16 chunks (256-byte rows): m mod 16. With m mod 8 for both, rows 8 apart
-// collided: bf16 GEMM consumers spent 37% and attention consumers 31% of
-// their LDS cycles on bank conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT against
-// SQ_LDS_IDX_ACTIVE); now 0, and 0 for fp32 as before.
+// 16 distinct 16-byte positions of a 256-byte bank span. A span holds 16 / QPR
+// rows, so rows that share their position within the span are 16 / QPR apart,
+// and the XOR must differ between them: (m / (16 / QPR)) mod QPR. 4 chunks
+// (64-byte rows): (m / 4) mod 4; 8 chunks (128-byte rows): (m / 2) mod 8;
+// 16 chunks (256-byte rows): m mod 16. With m mod 8 for 8 and 16 chunks, rows
+// 8 apart collided: bf16 GEMM consumers spent 37% and attention consumers 31%
+// of their LDS cycles on bank conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT
+// against SQ_LDS_IDX_ACTIVE); with (m / 2) mod 4 for 4 chunks, rows 8 apart
+// collided too (bf16 256 x 256 x 32: 34%).
 template <int QPR>
 __device__ __forceinline__ int row_swizzle(int m) {
-    if constexpr (QPR == 4) return (m >> 1) & 3;
+    if constexpr (QPR == 4) return (m >> 2) & 3;
     else if constexpr (QPR == 8) return (m >> 1) & 7;
     else return m & 15;
 }
