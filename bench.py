@@ -27,7 +27,9 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
                          in the input dtype, for context; two launches, so
                          its figure includes a separate ReLU pass
   copy.plain_device_copy = torch's own device-to-device copy of the same
-                         buffers, the bandwidth a plain copy kernel reaches
+                         buffers
+  copy.direct_baseline = this library's unstaged copy of the same buffers
+                         (no LDS ring, no roles), the ablation of staging
 Options select other workloads (--workload 4: ragged fp32, --workload 5:
 bf16 8192^3, --moe: a mixture-of-experts expert layer on the grouped GEMM,
 --attention: attention forward)
@@ -334,6 +336,18 @@ def run(args):
         result["copy"]["plain_device_copy"] = {"value": round(moved / p_kern / 1e9, 1), "unit": "GB/s",
                                                "kind": "torch Tensor.copy_ on the device"}
         result["copy"]["staged_over_plain"] = round(p_kern / c_kern, 4)
+        # the unstaged baseline of this library (no LDS ring, no roles: every lane moves 16-byte chunks
+        # through registers in a grid-stride loop, 4 in flight), timed the same way
+        direct_cfg = dict(flags=wsg.WSG_FLAG_DIRECT_COPY | (0 if args.copy_cached else wsg.WSG_FLAG_NONTEMPORAL))
+        direct = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=copy_stages, config=direct_cfg)  # noqa
+        for _ in range(args.warmup):
+            direct()
+        _, d_kern, _ = time_region(torch, direct, args.steps)
+        wsg.check_device_status()
+        result["copy"]["direct_baseline"] = {"value": round(moved / d_kern / 1e9, 1), "unit": "GB/s",
+                                             "kind": "unstaged copy (WSG_FLAG_DIRECT_COPY), 256 workgroups x 4 "
+                                                     "waves, 4 chunks of 16 bytes in flight per lane"}
+        result["copy"]["staged_over_direct"] = round(d_kern / c_kern, 4)
         # parity of the timed launch configuration, outside the timed regions: dst is overwritten
         # with a sentinel first, so only the staged copy can make it equal to src again
         copy_dst.fill_(-7.0)

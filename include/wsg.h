@@ -52,6 +52,7 @@ extern "C" {
 #define WSG_FLAG_GENERAL_PRODUCER 1 /* GEMM: force the register-staged producer (any shape) over the LDS-DMA one */
 #define WSG_FLAG_NONTEMPORAL 2      /* staged copy: streaming (non-temporal) loads and stores */
 #define WSG_FLAG_HOMOGENEOUS 4      /* GEMM: the baseline without roles (see below); producer_waves must be 0 */
+#define WSG_FLAG_DIRECT_COPY 8      /* staged copy: the baseline without staging (see staged_copy_ex) */
 
 /*
  * Launch configuration. A zero field means "choose the default". The
@@ -192,6 +193,12 @@ int staged_copy(const void *src, void *dst, size_t bytes, int stages);
  * MI355X: fewer concurrent streams of large tiles keep HBM busier; a
  * 1 GiB copy with 64 KiB slots runs at 6.0 TB/s with 192 workgroups and
  * 5.5 TB/s with 256). copy_workgroups > 0 sets G (capped at the tile count).
+ *
+ * WSG_FLAG_DIRECT_COPY selects the copy the staged one is measured against:
+ * no LDS ring and no roles, every lane moving 16-byte chunks src -> registers
+ * -> dst in a grid-stride loop with 4 chunks in flight (one 4-wave workgroup
+ * per CU unless copy_workgroups says otherwise; WSG_FLAG_NONTEMPORAL applies;
+ * stages is validated but not used). Same arguments, same result.
  */
 int staged_copy_ex(const void *src, void *dst, size_t bytes, int stages, const wsg_config *cfg);
 

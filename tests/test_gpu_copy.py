@@ -109,3 +109,17 @@ def test_copy_argument_errors(gpu):
     with pytest.raises(gpu.WsgError) as e:
         gpu.staged_copy_ex(x[:1024], x[2048:3072], stages=2, config=dict(copy_workgroups=-1))
     assert e.value.code == gpu.WSG_EINVAL
+
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 4095, 65537, 256 * 256 * 16 * 4 + 7, 3 * 1048576 + 9])
+@pytest.mark.parametrize("flags", [8, 8 | 2])  # WSG_FLAG_DIRECT_COPY, with and without streaming
+def test_direct_copy_baseline_sizes(gpu, n, flags):
+    """The unstaged baseline: same arguments, same bytes, guard bands intact, every tail size."""
+    _run_copy(gpu, _bytes(300 + n, n), 2, config=dict(flags=flags))
+
+
+@pytest.mark.parametrize("workgroups", [1, 7, 256, 1024])
+def test_direct_copy_grid_sizes(gpu, workgroups):
+    """Grid-stride loop: any grid covers every chunk exactly once (remainder loop included)."""
+    n = 256 * 256 * 16 * 3 + 4096 * 16 + 5
+    _run_copy(gpu, _bytes(400 + workgroups, n), 2, config=dict(flags=8 | 2, copy_workgroups=workgroups))

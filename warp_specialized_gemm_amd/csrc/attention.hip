@@ -279,7 +279,15 @@ __global__ void __launch_bounds__((P + NCW) * 64) attention_kernel(AttnArgs a) {
                 acc_o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], pf[ks], acc_o[c], 0, 0, 0);
         }
         wait_lgkm0();  // every read of the slot has landed
-        fl.arrive_empty(cs, cw == NCW - 1 ? NE - NCW + 1 : 1);
+        // Consumers sharing a SIMD drift apart (its matrix unit issues the
+        // older wave's MFMAs first): the ones releasing a slot in the later
+        // half raise their wave priority for the next tile (measured on
+        // MI355X, batch 4 x 32 heads x 4096^2: +3.6% non-causal, +3.5%
+        // causal, bit-identical).
+        if (fl.template arrive_empty_rank<NE>(cs, cw == NCW - 1 ? NE - NCW + 1 : 1) >= (uint32_t)(NE / 2))
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         if (++cs == S) {
             cs = 0;
             ++lap;

@@ -48,6 +48,7 @@ struct GemmPlan {
 struct CopyPlan {
     int P = 0, C = 0, tile = 0, stages = 0;
     int workgroups = 0;  // persistent grid size requested (0: the default policy)
+    bool direct = false;  // the unstaged baseline (WSG_FLAG_DIRECT_COPY)
     const void *kernel = nullptr;
     size_t lds_bytes = 0;
 };

@@ -152,42 +152,24 @@ __device__ __forceinline__ void flag_arrive(uint32_t addr, uint32_t n = 1u) {
         : "memory");
 }
 
-// The same arrival of N (an immediate) on a flag whose LDS address is
-// wave-uniform (an SGPR): address and count are moved into VGPRs inside the
-// assembly, so no register holds them between arrivals.
-template <uint32_t N = 1u>
-__device__ __forceinline__ void flag_arrive_uniform(uint32_t addr) {
-    uint64_t saved;
-    uint32_t va, vn;
-    asm volatile(
-        "s_mov_b64 %0, exec\n\t"
-        "s_mov_b64 exec, 1\n\t"
-        "v_mov_b32 %1, %3\n\t"
-        "v_mov_b32 %2, %4\n\t"
-        "ds_add_u32 %1, %2\n\t"
-        "s_mov_b64 exec, %0"
-        : "=&s"(saved), "=&v"(va), "=&v"(vn)
-        : "s"(addr), "n"(N)
-        : "memory");
-}
-
-// One arrival on a flag with E expected arrivals per phase (wave-uniform LDS
-// address), returning how many arrivals of the current phase preceded it
+// An arrival of n (1 unless a wave stands in for missing ones, as in
+// flag_arrive) on a flag with E expected arrivals per phase (wave-uniform LDS
+// address), returning the arrivals of the current phase that preceded it
 // (0 .. E - 1). The add returns a value, so its wait is inside the assembly.
 template <int E>
-__device__ __forceinline__ uint32_t flag_arrive_rank(uint32_t addr) {
+__device__ __forceinline__ uint32_t flag_arrive_rank(uint32_t addr, uint32_t n = 1u) {
     uint64_t saved;
     uint32_t va, vn, old;
     asm volatile(
         "s_mov_b64 %0, exec\n\t"
         "s_mov_b64 exec, 1\n\t"
         "v_mov_b32 %1, %4\n\t"
-        "v_mov_b32 %2, 1\n\t"
+        "v_mov_b32 %2, %5\n\t"
         "ds_add_rtn_u32 %3, %1, %2\n\t"
         "s_waitcnt lgkmcnt(0)\n\t"
         "s_mov_b64 exec, %0"
         : "=&s"(saved), "=&v"(va), "=&v"(vn), "=&v"(old)
-        : "s"(addr)
+        : "s"(addr), "s"(n)
         : "memory");
     return __builtin_amdgcn_readfirstlane(old) & (uint32_t)(E - 1);
 }
@@ -206,12 +188,9 @@ struct LdsFlags {
     __device__ bool wait_full(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {
         return flag_wait<E, RECORD>(full_flag(fb, s), parity, status, who, t);
     }
-    __device__ void arrive_empty_uniform(int s) const {
-        flag_arrive_uniform(__builtin_amdgcn_readfirstlane(empty_flag(fb, s)));
-    }
     template <int E>
-    __device__ uint32_t arrive_empty_rank(int s) const {
-        return flag_arrive_rank<E>(__builtin_amdgcn_readfirstlane(empty_flag(fb, s)));
+    __device__ uint32_t arrive_empty_rank(int s, uint32_t n = 1u) const {
+        return flag_arrive_rank<E>(__builtin_amdgcn_readfirstlane(empty_flag(fb, s)), n);
     }
     template <int E, bool RECORD = true>
     __device__ bool wait_empty(int s, uint32_t parity, unsigned *status, unsigned who, WaitTally &t) const {

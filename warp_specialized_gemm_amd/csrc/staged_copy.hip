@@ -155,7 +155,36 @@ __global__ void __launch_bounds__((P + C) * 64)
     }
 }
 
+// The copy without staging or roles, the baseline the staged copy is measured
+// against: every lane moves 16-byte chunks src -> VGPRs -> dst in a
+// grid-stride loop, U chunks in flight per lane (consecutive lanes, consecutive
+// chunks), then the bytes past the last whole chunk. No LDS and no flags.
+template <int U, bool NT>
+__global__ void __launch_bounds__(256) direct_copy_kernel(const unsigned char *__restrict__ src,
+                                                          unsigned char *__restrict__ dst, uint64_t bytes) {
+    const u32x4 *s = reinterpret_cast<const u32x4 *>(src);
+    u32x4 *d = reinterpret_cast<u32x4 *>(dst);
+    const uint64_t chunks = bytes >> 4;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (U - 1) * stride < chunks; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(s + i + u * stride) : s[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (NT) __builtin_nontemporal_store(v[u], d + i + u * stride);
+            else d[i + u * stride] = v[u];
+        }
+    }
+    for (; i < chunks; i += stride) d[i] = s[i];
+    const uint64_t tail = bytes & 15u;
+    if (blockIdx.x == 0 && threadIdx.x < tail) dst[(chunks << 4) + threadIdx.x] = src[(chunks << 4) + threadIdx.x];
+}
+
 namespace {
+
+constexpr int kDirectUnroll = 4;  // chunks in flight per lane
 
 struct CopyVariant {
     int P, C, tile;
@@ -189,6 +218,22 @@ int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo 
         *err = "copy_workgroups must be >= 0";
         return WSG_EINVAL;
     }
+    if (stages < 1) {
+        *err = "stages must be >= 1";
+        return WSG_EINVAL;
+    }
+    if (cfg && (cfg->flags & WSG_FLAG_DIRECT_COPY)) {
+        // the unstaged baseline: no ring, no roles (stages is not used)
+        plan->direct = true;
+        plan->P = plan->C = 0;
+        plan->tile = 16;
+        plan->stages = stages;
+        plan->kernel = nt ? reinterpret_cast<const void *>(&direct_copy_kernel<kDirectUnroll, true>)
+                          : reinterpret_cast<const void *>(&direct_copy_kernel<kDirectUnroll, false>);
+        plan->lds_bytes = 0;
+        plan->workgroups = workgroups;
+        return WSG_OK;
+    }
     if (!cfg) {
         // defaults: the largest slot that lets `stages` slots share 128 KiB of
         // LDS, streamed past the caches (the fastest measured settings)
@@ -197,10 +242,6 @@ int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo 
         while (tile > 8192 && (size_t)stages * (size_t)tile > 131072) tile /= 2;
     } else if (!tile) {
         tile = 65536;
-    }
-    if (stages < 1) {
-        *err = "stages must be >= 1";
-        return WSG_EINVAL;
     }
     if (stages > kMaxStages) {
         *err = "stages above the flag area's limit of " + std::to_string(kMaxStages);
@@ -238,6 +279,25 @@ int plan_copy(size_t bytes, int stages, const wsg_config *cfg, const DeviceInfo 
 int launch_copy(const LaunchCtx &ctx, const CopyPlan &plan, const void *src, void *dst, size_t bytes,
                 std::string *err) {
     if (bytes == 0) return WSG_OK;
+    if (plan.direct) {
+        // one 4-wave workgroup per CU by default (measured on MI355X: the
+        // fastest plain-copy launch shape, 256 workgroups x 4 waves with 4
+        // loads in flight per lane)
+        const uint64_t lanes_needed = (bytes / 16 + 255) / 256;
+        uint64_t grid = plan.workgroups > 0 ? (uint64_t)plan.workgroups : (uint64_t)ctx.dev.cu_count;
+        if (grid > lanes_needed) grid = lanes_needed;
+        if (grid < 1) grid = 1;
+        const unsigned char *s = static_cast<const unsigned char *>(src);
+        unsigned char *d = static_cast<unsigned char *>(dst);
+        uint64_t nb = bytes;
+        void *args[] = {&s, &d, &nb};
+        hipError_t e = hipLaunchKernel(plan.kernel, dim3((unsigned)grid), dim3(256), args, 0, ctx.stream);
+        if (e != hipSuccess) {
+            *err = std::string("direct copy launch: ") + hipGetErrorString(e);
+            return WSG_ELAUNCH;
+        }
+        return WSG_OK;
+    }
     const uint64_t ntiles = (bytes + (uint64_t)plan.tile - 1) / (uint64_t)plan.tile;
     const int threads = (plan.P + plan.C) * 64;
     const int rc = prepare_kernel(plan.kernel, ctx.dev, err);
