@@ -252,6 +252,7 @@ def run(args):
             "tile": [resolved["BM"], resolved["BN"], resolved["BK"]],
             "producer_waves": resolved["producer_waves"], "consumer_waves": resolved["consumer_waves"],
             "group_k": resolved["group_k"], "homogeneous": bool(resolved["flags"] & wsg.WSG_FLAG_HOMOGENEOUS),
+            "stream_k": bool(resolved["flags"] & wsg.WSG_FLAG_STREAM_K),
             "input": "uniform[-1,1) splitmix64" if dtype == "fp32" else "N(0,1)*0.1 rounded to bf16",
         },
     }

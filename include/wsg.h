@@ -53,6 +53,8 @@ extern "C" {
 #define WSG_FLAG_NONTEMPORAL 2      /* staged copy: streaming (non-temporal) loads and stores */
 #define WSG_FLAG_HOMOGENEOUS 4      /* GEMM: the baseline without roles (see below); producer_waves must be 0 */
 #define WSG_FLAG_DIRECT_COPY 8      /* staged copy: the baseline without staging (see staged_copy_ex) */
+#define WSG_FLAG_STREAM_K 16        /* fp32 GEMM: always give the last round of tiles a stream-K split (see below) */
+#define WSG_FLAG_NO_STREAM_K 32     /* fp32 GEMM: never split tiles along K: one workgroup per output tile */
 
 /*
  * Launch configuration. A zero field means "choose the default". The
@@ -121,7 +123,8 @@ int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
  * One launch covers every expert's tiles (each expert's rows are tiled on
  * their own, so its last tile row is ragged); every expert's rows equal what
  * gemm_bias_relu_ex returns for that expert's slice with the same explicit
- * configuration.
+ * configuration and WSG_FLAG_NO_STREAM_K (grouped launches take no stream-K
+ * tail).
  */
 int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, int64_t N, int64_t K,
                               const void *A, const void *B, const void *bias, float *C, int stages,
@@ -136,6 +139,20 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  * stages >= 2 loads tile t + S - 1 while tile t is computed, with one barrier
  * per tile. It needs the LDS-DMA alignment (K and N multiples of 16 bytes,
  * 16-byte aligned A and B; else WSG_EUNSUPPORTED).
+ *
+ * Stream-K tail (fp32, wave-specialized LDS-DMA kernels; not from the pages,
+ * which launch one workgroup per output tile): when the tiles fill at least
+ * one round of the device's resident workgroups and the last round is at most
+ * 90% full, the launch is a persistent grid of one round. Each workgroup takes
+ * its whole-tile rounds, then an equal share of the remaining tiles' K steps;
+ * a tile split between workgroups is summed in a fixed order (the piece with
+ * k = 0 first, then the others by increasing k), so results do not depend on
+ * timing but differ in rounding from the one-workgroup-per-tile launch.
+ * WSG_FLAG_STREAM_K forces the split (with no ragged round, the last full
+ * round is split); WSG_FLAG_NO_STREAM_K forbids it. The partial sums and
+ * counters live in a device workspace the library allocates on first need
+ * per (device, stream) and keeps until the process ends; growing it waits
+ * for that stream. A failed wait on another piece sets WSG_STATUS_TIMEOUT.
  */
 
 /*
@@ -168,7 +185,9 @@ int attention_fwd(int64_t batch, int64_t heads, int64_t Sq, int64_t Skv, int64_t
 /*
  * The configuration gemm_bias_relu_ex would launch for these arguments,
  * written to *out, after the same validation (returns its error code).
- * Writes the resolved tile and wave counts; no device work.
+ * Writes the resolved tile and wave counts; no device work. flags reports
+ * WSG_FLAG_GENERAL_PRODUCER, WSG_FLAG_HOMOGENEOUS and WSG_FLAG_STREAM_K for
+ * the kernel that would run.
  */
 int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stages, const wsg_config *cfg,
                             wsg_config *out);

@@ -145,7 +145,8 @@ def test_each_expert_equals_the_plain_gemm_bit_for_bit(gpu):
     start = 0
     for e, n in enumerate(rows):
         if n:
-            Ce = run_f32(gpu, A[start:start + n], B[e], bias[e], stages=2, config=cfg, guards=False)
+            Ce = run_f32(gpu, A[start:start + n], B[e], bias[e], stages=2, config=dict(cfg, flags=32),  # NO_STREAM_K
+                         guards=False)
             assert np.array_equal(C[start:start + n].view(np.uint32), Ce.view(np.uint32)), "expert %d" % e
         start += n
 

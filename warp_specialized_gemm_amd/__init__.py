@@ -23,7 +23,8 @@ __all__ = [
     "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
     "set_stream", "get_stream", "status_message",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
-    "WSG_FLAG_HOMOGENEOUS", "WSG_FLAG_DIRECT_COPY", "WSG_MAX_GROUPS",
+    "WSG_FLAG_HOMOGENEOUS", "WSG_FLAG_DIRECT_COPY", "WSG_FLAG_STREAM_K", "WSG_FLAG_NO_STREAM_K",
+    "WSG_MAX_GROUPS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,8 @@ WSG_FLAG_GENERAL_PRODUCER = 1
 WSG_FLAG_NONTEMPORAL = 2
 WSG_FLAG_HOMOGENEOUS = 4
 WSG_FLAG_DIRECT_COPY = 8
+WSG_FLAG_STREAM_K = 16
+WSG_FLAG_NO_STREAM_K = 32
 WSG_MAX_GROUPS = 64
 WSG_STATUS_TIMEOUT = 1
 WSG_STATUS_COPY = 2

@@ -71,6 +71,32 @@ int device_info(wsg::DeviceInfo *out) {
     return WSG_OK;
 }
 
+// Stream-K workspaces, allocated on first need and grown as needed, one per
+// (device, stream): launches on one stream run in order, so they may share
+// it; launches on different streams may overlap, so they may not.
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+
+int sk_workspace(int dev, hipStream_t stream, size_t bytes, void **out) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto &w = g_ws[{dev, stream}];
+    if (w.second < bytes) {
+        if (w.first) {
+            // the previous workspace may still be in use by queued launches
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e == hipSuccess) e = hipFree(w.first);
+            if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("stream-K workspace release: ") + hipGetErrorString(e));
+            w = {nullptr, 0};
+        }
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("stream-K workspace: hipMalloc: ") + hipGetErrorString(e));
+        w = {p, bytes};
+    }
+    *out = w.first;
+    return WSG_OK;
+}
+
 std::mutex g_kernel_mu;
 std::map<std::pair<int, const void *>, bool> g_prepared;
 std::map<std::tuple<int, const void *, int, size_t>, int> g_occupancy;
@@ -123,7 +149,13 @@ int gemm_impl(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     std::string err;
     rc = wsg::plan_gemm(dtype, M, N, K, A, B, stages, cfg, ctx.dev, &plan, &err);
     if (rc != WSG_OK) return fail(rc, err);
-    rc = wsg::launch_gemm(ctx, plan, M, N, K, A, B, bias, C, &err);
+    const wsg::SkShape sk = wsg::plan_stream_k(plan, M, N, K, cfg ? cfg->flags : 0, ctx.dev);
+    void *ws = nullptr;
+    if (sk.use) {
+        rc = sk_workspace(ctx.dev.device, ctx.stream, sk.bytes(), &ws);
+        if (rc != WSG_OK) return rc;
+    }
+    rc = wsg::launch_gemm(ctx, plan, M, N, K, A, B, bias, C, &sk, ws, &err);
     if (rc != WSG_OK) return fail(rc, err);
     return ok();
 }
@@ -305,7 +337,8 @@ int wsg_gemm_resolve_config(int dtype, int64_t M, int64_t N, int64_t K, int stag
     out->producer_waves = plan.v->P;
     out->consumer_waves = plan.v->CWM * plan.v->CWN;
     out->copy_tile_bytes = 0;
-    out->flags = (plan.v->dma ? 0 : WSG_FLAG_GENERAL_PRODUCER) | (plan.v->P == 0 ? WSG_FLAG_HOMOGENEOUS : 0);
+    out->flags = (plan.v->dma ? 0 : WSG_FLAG_GENERAL_PRODUCER) | (plan.v->P == 0 ? WSG_FLAG_HOMOGENEOUS : 0) |
+                 (wsg::plan_stream_k(plan, M, N, K, cfg ? cfg->flags : 0, dev).use ? WSG_FLAG_STREAM_K : 0);
     out->group_k = plan.v->GK;
     return ok();
 }

@@ -63,6 +63,10 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     unsigned *status;
     unsigned long long *stats;  // wait statistics, or null
+    // stream-K launches only (kernels built with SK): see sk_unit
+    int dp_tiles, sk_tiles, workers;
+    float *part;      // one partial tile (BM x BN fp32) per worker
+    unsigned *cnt;    // per stream-K tile and consumer wave: contributor pieces done
 };
 
 // Each XCD takes a contiguous run of logical tiles (xcd_linear), walked in
@@ -297,6 +301,136 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 }
 
 // ----------------------------------------------------------------------------
+// Stream-K tail (fp32 kernels built with SK). When the output tiles do not
+// fill a whole number of rounds of the persistent grid (`workers` workgroups,
+// as many as the device holds at once), the last, partial round would leave
+// CUs idle: 480 tiles of
+// 256 x 128 on 256 CUs run as a full round and a round of 224. Instead, each
+// worker w first computes data-parallel tiles w, w + workers, ... (dp_tiles
+// of them in all, whole rounds only), then an equal contiguous share of the
+// remaining sk_tiles x T k-tile steps (tile-major, k ascending). A share is
+// shorter than a tile, so it covers at most two tiles: the end of one (a
+// "contributor" piece) and the start of the next (its "owner" piece, k from
+// 0). A contributor stores its fp32 accumulators in the worker's partial
+// slot, then counts itself done on the tile; the owner waits for the tile's
+// other pieces, adds their partials in piece order (so the sum order is fixed
+// whoever finishes first) and runs the epilogue. The ring flags carry on
+// across a worker's units: producers stream them back to back.
+// ----------------------------------------------------------------------------
+struct SkUnit {
+    int tile;      // logical tile index (before the tile-row swizzle)
+    int kb, ke;    // k-tile range [kb, ke)
+    int kind;      // 0: the whole tile; 1: owner piece; 2: contributor piece
+    int sk_tile;   // index among the stream-K tiles (kinds 1 and 2)
+    int first, npieces;  // worker of the tile's first piece, pieces of the tile
+};
+
+// Worker whose share of the Z stream-K steps holds step i: shares are
+// [w Z / G, (w + 1) Z / G), so it is the largest w with w Z / G <= i.
+__device__ __forceinline__ int sk_worker_of(int64_t i, int64_t Z, int G) { return (int)(((i + 1) * G - 1) / Z); }
+
+// Unit u of worker w (wave-uniform); false past the last one.
+__device__ __forceinline__ bool sk_unit(const GemmArgs &a, int T, int w, int u, SkUnit &out) {
+    const int G = a.workers;
+    const int rounds = a.dp_tiles / G;
+    if (u < rounds) {
+        out = SkUnit{u * G + w, 0, T, 0, -1, w, 1};
+        return true;
+    }
+    int idx = u - rounds;
+    // with fewer steps than workers only the first Z workers take one each:
+    // every share is then non-empty, so the workers between a tile's first
+    // and last piece all hold a piece of it
+    const int64_t Z = (int64_t)a.sk_tiles * T;
+    const int Gs = (int)min((int64_t)G, Z);
+    if (w >= Gs) return false;
+    int64_t i = (int64_t)w * Z / Gs;
+    const int64_t e = (int64_t)(w + 1) * Z / Gs;
+    while (i < e) {
+        const int64_t tau = i / T;
+        const int kb = (int)(i - tau * T);
+        const int ke = (int)min((int64_t)T, e - tau * T);
+        if (idx == 0) {
+            const int wf = sk_worker_of(tau * T, Z, Gs), wl = sk_worker_of(tau * T + T - 1, Z, Gs);
+            out.tile = a.dp_tiles + (int)tau;
+            out.kb = kb;
+            out.ke = ke;
+            out.sk_tile = (int)tau;
+            out.first = wf;
+            out.npieces = wl - wf + 1;
+            out.kind = out.npieces == 1 ? 0 : (kb == 0 ? 1 : 2);
+            return true;
+        }
+        --idx;
+        i = tau * T + ke;
+    }
+    return false;
+}
+
+// Producer of a stream-K worker: the LDS-DMA producer above, run over every
+// k-tile of the worker's units in order, with one in-flight window across
+// them.
+template <int BM, int BN, int BK, int ES, int P, int NCW, int kGroupRows, typename Flags>
+__device__ __forceinline__ void produce_sk(const GemmArgs &a, unsigned char *ring, const Flags &fl, int wave, int lane,
+                                           int T, int w) {
+    constexpr int A_BYTES = BM * BK * ES, SLOT = A_BYTES + BK * BN * ES;
+    using AD = ADma<BM, BK, ES, P>;
+    using BD = BDma<BN, BK, ES, P>;
+    constexpr int NL = AD::NL + BD::NL;
+    static_assert(NL <= 63, "one tile's loads must fit vmcnt");
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int S = a.S;
+    const int D = max(1, min(S - 1, 63 / NL));
+    int s = 0, inflight = 0, ps = 0;
+    uint32_t lap = 0;
+    WaitTally tally;
+    SkUnit un;
+    for (int u = 0; sk_unit(a, T, w, u, un); ++u) {
+        int tm, tn;
+        swizzle_tile<kGroupRows>(un.tile, a.tiles_m, a.tiles_n, tm, tn);
+        const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+        const int rows_valid = (int)min((int64_t)BM, M - m0);
+        const unsigned char *A_rows = a.A + (size_t)m0 * (size_t)K * ES;
+        AD ad;
+        BD bd;
+        ad.init(wave, lane, K, rows_valid);
+        bd.init(wave, lane, N, n0);
+        for (int t = un.kb; t < un.ke; ++t) {
+            if (inflight == D) {
+                wait_vmcnt_dyn((D - 1) * NL);
+                fl.arrive_full(ps);
+                if (++ps == S) ps = 0;
+                --inflight;
+            }
+            if (!fl.template wait_empty<NCW>(s, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+            const int64_t k0 = (int64_t)t * BK;
+            unsigned char *slot = ring + (size_t)s * SLOT;
+            ad.issue(slot, wave, A_rows, rows_valid, K, k0);
+            bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
+            ++inflight;
+            if (++s == S) {
+                s = 0;
+                ++lap;
+            }
+        }
+    }
+    while (inflight > 0) {
+        wait_vmcnt_dyn((inflight - 1) * NL);
+        fl.arrive_full(ps);
+        if (++ps == S) ps = 0;
+        --inflight;
+    }
+    publish_tally(a.stats ? a.stats + kStatGemmProducer : nullptr, tally);
+}
+
+// Ring position of a consumer between units: the slot and lap of the next
+// tile it reads.
+struct RingPos {
+    int s = 0;
+    uint32_t lap = 0;
+};
+
+// ----------------------------------------------------------------------------
 // Consumer walk over the ring, a group at a time (the fp32 kernels, whose
 // 256-register consumers spill under the per-tile walk below). The K loop is
 // cut into U = T * KG groups of 16 k; the fragments of group u + 1 are read
@@ -315,17 +449,18 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 // 4096^3 default, +2.6 to +5.5% for the bf16 configurations).
 template <int KG, int P, typename Frag, int IL = 0, typename Flags, typename Read, typename Mma>
 __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, int slot_bytes, const Flags &fl,
-                                             unsigned *status, WaitTally &tally, Read read, Mma mma) {
+                                             unsigned *status, WaitTally &tally, Read read, Mma mma,
+                                             RingPos &pos) {
     const int U = T * KG;
     if (U == 0) return true;
     Frag f0, f1;
-    int rs = 0, rg = 0;  // slot and group of the latest read
-    uint32_t rlap = 0;
-    int cs = 0;          // slot being consumed
-    uint32_t peek = 0;   // early value of the next tile's full flag
-    if (!fl.template wait_full<P>(0, 0u, status, kStatusGemm, tally)) return false;
-    read(f0, ring, 0);
-    if (KG == 1 && U > 1) peek = fl.peek_full(S > 1 ? 1 : 0);
+    int rs = pos.s, rg = 0;  // slot and group of the latest read
+    uint32_t rlap = pos.lap;
+    int cs = pos.s;          // slot being consumed
+    uint32_t peek = 0;       // early value of the next tile's full flag
+    if (!fl.template wait_full<P>(pos.s, pos.lap & 1u, status, kStatusGemm, tally)) return false;
+    read(f0, ring + (size_t)pos.s * slot_bytes, 0);
+    if (KG == 1 && U > 1) peek = fl.peek_full(pos.s + 1 == S ? 0 : pos.s + 1);
     bool alive = true;
     auto step = [&](int u, Frag &cur, Frag &nxt) {
         wait_lgkm0();  // the reads of group u (and the early flag value) have landed
@@ -388,6 +523,9 @@ __device__ __forceinline__ bool consume_ring(int T, int S, unsigned char *ring, 
         step(u, f0, f1);
         if (alive && u + 1 < U) step(u + 1, f1, f0);
     }
+    // the next tile after the last one read
+    pos.s = rs + 1 == S ? 0 : rs + 1;
+    pos.lap = pos.s == 0 ? rlap + 1 : rlap;
     return alive;
 }
 
@@ -650,8 +788,9 @@ __device__ __forceinline__ void sync_loop(const GemmArgs &a, unsigned char *ring
 // ----------------------------------------------------------------------------
 // fp32 kernel
 // ----------------------------------------------------------------------------
-template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA, bool GR>
+template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA, bool GR, bool SK = false>
 __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename KernelArgs<GR>::type ka) {
+    static_assert(!SK || (P > 0 && DMA && !GR), "stream-K: specialized LDS-DMA kernels, ordinary launches");
     GemmArgs &a = gemm_args(ka);
     constexpr int NCW = CWM * CWN;
     constexpr int WTM = BM / CWM, WTN = BN / CWN;
@@ -668,8 +807,10 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
 
     const LdsFlags fl = init_flags(lds);
 
-    int tm, tn;
-    resolve_tile<(8 * BN / BM > 0 ? 8 * BN / BM : 1), BM, 4>(ka, tm, tn);
+    constexpr int kGroupRows = 8 * BN / BM > 0 ? 8 * BN / BM : 1;
+    int tm = 0, tn = 0, w = 0;  // tile (ordinary launches) or stream-K worker
+    if constexpr (SK) w = xcd_linear(blockIdx.x, a.workers);
+    else resolve_tile<kGroupRows, BM, 4>(ka, tm, tn);
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int T = (int)((K + BK - 1) / BK);
@@ -677,7 +818,8 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
 
     if constexpr (P > 0) {
         if (wave < P) {
-            produce<BM, BN, BK, 4, P, NCW, DMA>(a, ring, fl, wave, lane, m0, n0, T);
+            if constexpr (SK) produce_sk<BM, BN, BK, 4, P, NCW, kGroupRows>(a, ring, fl, wave, lane, T, w);
+            else produce<BM, BN, BK, 4, P, NCW, DMA>(a, ring, fl, wave, lane, m0, n0, T);
             return;
         }
     }
@@ -732,50 +874,160 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[i][jj], f.b[j][jj], acc[i][j], 0, 0, 0);
     };
 
+    // epilogue: C = relu(acc + bias[n]); lane (li, q) holds column li and rows
+    // 4q + r of each 16x16 block
+    auto epilogue = [&](int64_t m0, int64_t n0) {
+        const float *bias = reinterpret_cast<const float *>(a.bias) + n0;
+        float *ctile = a.C + m0 * N + n0;
+        const int rbase = wr * WTM + 4 * q, cbase = wc * WTN + li;
+        const int rows_valid = (int)min((int64_t)BM, M - m0), cols_valid = (int)min((int64_t)BN, N - n0);
+        // all bias loads first: stores count in the same counter, so a bias load
+        // waited for between stores would also wait for every store before it
+        float bv[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = cbase + 16 * j < cols_valid ? bias[cbase + 16 * j] : 0.0f;
+        if (rows_valid == BM && cols_valid == BN) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = cbase + 16 * j;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ctile[(int64_t)(rbase + 16 * i + r) * N + col] = relu_f32(acc[i][j][r] + bv[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = cbase + 16 * j;
+                if (col >= cols_valid) continue;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = rbase + 16 * i + r;
+                        if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv[j]);
+                    }
+            }
+        }
+    };
+
+    if constexpr (SK) {
+        // stream-K worker: every unit's k range through the same ring, then
+        // its epilogue, partial store or fixup
+        constexpr int ACC = FM * FN * 4;  // accumulators per lane
+        WaitTally tally;
+        RingPos pos;
+        SkUnit un;
+        bool ok = true;
+        for (int u = 0; ok && sk_unit(a, T, w, u, un); ++u) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            ok = consume_ring<KG, P, Frag, FM + 4 * FN>(un.ke - un.kb, S, ring, SLOT, fl, a.status, tally, read, mma,
+                                                         pos);
+            if (!ok) break;
+            int utm, utn;
+            swizzle_tile<kGroupRows>(un.tile, a.tiles_m, a.tiles_n, utm, utn);
+            unsigned *cnt = a.cnt + (size_t)un.sk_tile * NCW + cw;
+            // The lane index through an empty asm: addresses derived from it
+            // are formed here, not hoisted out of the unit loop where they
+            // would stay live (and spill) through the K loop.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            if (un.kind == 2) {
+                // contributor: this worker's partial slot, lane-interleaved
+                // (register r of lane l at r * 64 + l; one lane offset, the
+                // register's in the scalar offset), then count it done
+                const __amdgpu_buffer_rsrc_t rp =
+                    make_rsrc(a.part + ((size_t)w * NCW + cw) * (64 * ACC), 64 * ACC * 4);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][e]), rp, 4 * ln,
+                                                                  ((i * FN + j) * 4 + e) * 256, 0);
+                if (ln == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
+            if (un.kind == 1) {
+                // owner: wait for the other pieces, add them in piece order
+                const uint32_t need = (uint32_t)(un.npieces - 1);
+                uint32_t spins = 0;
+                while (__builtin_amdgcn_readfirstlane(
+                           __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins > kSpinLimit) {
+                        ok = false;
+                        break;
+                    }
+                }
+                if (!ok) break;
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                for (int p = 1; p < un.npieces; ++p) {
+                    const __amdgpu_buffer_rsrc_t rp =
+                        make_rsrc(a.part + ((size_t)(un.first + p) * NCW + cw) * (64 * ACC), 64 * ACC * 4);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[i][j][e] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                    rp, 4 * ln, ((i * FN + j) * 4 + e) * 256, 0));
+                }
+                if (ln == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // epilogue through a buffer resource at the tile's origin (as in
+            // the single-fragment bf16 kernels): one lane offset, each store's
+            // row and column block added into a temporary; rows past M fall
+            // outside the range (which covers the VGPR offset), columns past
+            // N are masked per lane
+            const int64_t um0 = (int64_t)utm * BM, un0 = (int64_t)utn * BN;
+            const int rbase = wr * WTM + 4 * (ln >> 4), cbase = wc * WTN + (ln & 15);
+            const int rows_valid = (int)min((int64_t)BM, M - um0), cols_valid = (int)min((int64_t)BN, N - un0);
+            const float *bias = reinterpret_cast<const float *>(a.bias) + un0;
+            float bv[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bv[j] = cbase + 16 * j < cols_valid ? bias[cbase + 16 * j] : 0.0f;
+            const __amdgpu_buffer_rsrc_t rc =
+                make_rsrc(a.C + um0 * N + un0, (uint32_t)(((int64_t)(rows_valid - 1) * N + cols_valid) * 4));
+            const uint32_t voff = (uint32_t)(rbase * (int)N + cbase) * 4u;
+            const uint32_t row4 = (uint32_t)N * 4u;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if (cbase + 16 * j >= cols_valid) continue;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __float_as_uint(relu_f32(acc[i][j][r] + bv[j])), rc,
+                            voff + (uint32_t)(16 * i + r) * row4 + 64u * j, 0, 0);
+            }
+        }
+        if (!ok) {
+            atomicOr(a.status, kStatusTimeout | kStatusGemm);
+            return;
+        }
+        publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
+        return;
+    }
+
     if constexpr (P == 0) {
         static_assert(DMA, "the homogeneous loop loads by LDS-DMA");
         sync_loop<BM, BN, BK, 4, NCW, KG, Frag>(a, ring, cw, lane, m0, n0, T, read, mma);
     } else {
         WaitTally tally;
-        if (!consume_ring<KG, P, Frag, FM + 4 * FN>(T, S, ring, SLOT, fl, a.status, tally, read, mma)) return;
+        RingPos pos;
+        if (!consume_ring<KG, P, Frag, FM + 4 * FN>(T, S, ring, SLOT, fl, a.status, tally, read, mma, pos)) return;
         publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
     }
 
-    // epilogue: C = relu(acc + bias[n]); lane (li, q) holds column li and rows
-    // 4q + r of each 16x16 block
-    const float *bias = reinterpret_cast<const float *>(a.bias) + n0;
-    float *ctile = a.C + m0 * N + n0;
-    const int rbase = wr * WTM + 4 * q, cbase = wc * WTN + li;
-    const int rows_valid = (int)min((int64_t)BM, M - m0), cols_valid = (int)min((int64_t)BN, N - n0);
-    // all bias loads first: stores count in the same counter, so a bias load
-    // waited for between stores would also wait for every store before it
-    float bv[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bv[j] = cbase + 16 * j < cols_valid ? bias[cbase + 16 * j] : 0.0f;
-    if (rows_valid == BM && cols_valid == BN) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = cbase + 16 * j;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    ctile[(int64_t)(rbase + 16 * i + r) * N + col] = relu_f32(acc[i][j][r] + bv[j]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = cbase + 16 * j;
-            if (col >= cols_valid) continue;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = rbase + 16 * i + r;
-                    if (row < rows_valid) ctile[(int64_t)row * N + col] = relu_f32(acc[i][j][r] + bv[j]);
-                }
-        }
-    }
+    epilogue(m0, n0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1023,14 +1275,24 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
 
 namespace {
 
+// The stream-K instantiation of an fp32 variant: built for the specialized
+// LDS-DMA kernels only.
+template <int BM, int BN, int BK, int P, int CWM, int CWN, bool DMA>
+constexpr const void *f32_sk_kernel() {
+    if constexpr (P > 0 && DMA) return reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA,
+                                                                                        false, true>);
+    else return nullptr;
+}
+
 #define WSG_F32(BM, BN, BK, P, CWM, CWN, DMA)                                                              \
     {WSG_FP32, BM, BN, BK, P, CWM, CWN, DMA, 16,                                                           \
      reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA, false>),                \
-     reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA, true>)}
+     reinterpret_cast<const void *>(&gemm_f32_kernel<BM, BN, BK, P, CWM, CWN, DMA, true>),                 \
+     f32_sk_kernel<BM, BN, BK, P, CWM, CWN, DMA>()}
 #define WSG_BF(BM, BN, BK, P, CWM, CWN, DMA, GK)                                                           \
     {WSG_BF16, BM, BN, BK, P, CWM, CWN, DMA, GK,                                                           \
      reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK, false>),           \
-     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK, true>)}
+     reinterpret_cast<const void *>(&gemm_bf16_kernel<BM, BN, BK, P, CWM, CWN, DMA, GK, true>), nullptr}
 
 // When the caller leaves fields at 0, the first variant (in this order) whose
 // tile matches the size class and whose ring fits in LDS wins.
@@ -1235,13 +1497,63 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K, const void *A, const void *B
 
 }  // namespace
 
+// Zero the stream-K counters before a launch (a kernel, not a memset, so that
+// the two launches can be captured in a graph).
+__global__ void sk_clear_kernel(unsigned *cnt, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) cnt[i] = 0u;
+}
+
+SkShape plan_stream_k(const GemmPlan &plan, int64_t M, int64_t N, int64_t K, int flags, const DeviceInfo &dev) {
+    SkShape sk;
+    const GemmVariant &v = *plan.v;
+    if (!v.sk_kernel || (flags & WSG_FLAG_NO_STREAM_K) || M == 0 || N == 0 || K == 0) return sk;
+    // the buffer-store epilogue and partial slots use 32-bit offsets
+    if ((int64_t)v.BM * N * 4 >= 0x7FFFFFFF) return sk;
+    const int threads = (v.P + v.CWM * v.CWN) * 64;
+    const int64_t workers = (int64_t)dev.cu_count * blocks_per_cu(v.sk_kernel, dev, threads, plan.lds_bytes);
+    const int64_t tiles = plan.tiles_m * plan.tiles_n;
+    const int64_t rounds = tiles / workers, rem = tiles % workers;
+    if (!(flags & WSG_FLAG_STREAM_K)) {
+        // a tail worth spreading: at least one whole round, and a last round
+        // at most 90% full (480 tiles on 256 CUs: 224 in the last round)
+        if (rounds < 1 || rem == 0 || rem * 10 > workers * 9) return sk;
+    }
+    if (workers * (int64_t)v.BM * v.BN * 4 >= 0x7FFFFFFF) return sk;
+    sk.use = true;
+    sk.workers = (int)workers;
+    sk.dp_tiles = rem == 0 ? (rounds - 1) * workers : rounds * workers;  // forced with no tail: split the last round
+    sk.sk_tiles = tiles - sk.dp_tiles;
+    sk.part_bytes = (size_t)workers * v.BM * v.BN * 4;
+    sk.cnt_bytes = ((size_t)sk.sk_tiles * v.CWM * v.CWN * 4 + 255) / 256 * 256;
+    return sk;
+}
+
 int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N, int64_t K, const void *A,
-                const void *B, const void *bias, float *C, std::string *err) {
+                const void *B, const void *bias, float *C, const SkShape *sk, void *ws, std::string *err) {
     if (M == 0 || N == 0) return WSG_OK;
     GemmArgs args = make_args(M, N, K, A, B, bias, C);
     fill_common(ctx, plan, args);
     args.tiles_m = (int)plan.tiles_m;
-    return launch_with(ctx, plan, plan.v->kernel, &args, plan.tiles_m * plan.tiles_n, err);
+    args.dp_tiles = args.sk_tiles = args.workers = 0;
+    args.part = nullptr;
+    args.cnt = nullptr;
+    if (!sk || !sk->use) return launch_with(ctx, plan, plan.v->kernel, &args, plan.tiles_m * plan.tiles_n, err);
+    args.dp_tiles = (int)sk->dp_tiles;
+    args.sk_tiles = (int)sk->sk_tiles;
+    args.workers = sk->workers;
+    args.part = static_cast<float *>(ws);
+    args.cnt = reinterpret_cast<unsigned *>(static_cast<unsigned char *>(ws) + sk->part_bytes);
+    const int ncnt = (int)(sk->sk_tiles * plan.v->CWM * plan.v->CWN);
+    unsigned *cnt = args.cnt;
+    void *cargs[] = {&cnt, (void *)&ncnt};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sk_clear_kernel), dim3((ncnt + 255) / 256),
+                                   dim3(256), cargs, 0, ctx.stream);
+    if (e != hipSuccess) {
+        *err = std::string("stream-K counter clear: ") + hipGetErrorString(e);
+        return WSG_ELAUNCH;
+    }
+    return launch_with(ctx, plan, plan.v->sk_kernel, &args, sk->workers, err);
 }
 
 int launch_grouped_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int groups, const int64_t *group_rows, int64_t N,

@@ -36,6 +36,7 @@ struct GemmVariant {
     int GK;       // consumer k per fragment group
     const void *kernel;          // ordinary launch
     const void *grouped_kernel;  // the same kernel for a grouped (mixture-of-experts) launch
+    const void *sk_kernel;       // the same kernel as a stream-K persistent grid, or null if not built
 };
 
 struct GemmPlan {
@@ -67,8 +68,25 @@ int blocks_per_cu(const void *kernel, const DeviceInfo &dev, int threads, size_t
 // Fill `plan` for the arguments; returns WSG_OK or an error code with `err` set.
 int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, int stages,
               const wsg_config *cfg, const DeviceInfo &dev, GemmPlan *plan, std::string *err);
+// Stream-K tail of an ordinary launch (fp32 specialized LDS-DMA kernels): a
+// persistent grid of `workers` workgroups computes dp_tiles whole tiles (whole
+// rounds) and splits the sk_tiles left over evenly along K. Its workspace:
+// part_bytes of partial tiles (one per worker), then cnt_bytes of counters.
+struct SkShape {
+    bool use = false;
+    int workers = 0;
+    int64_t dp_tiles = 0, sk_tiles = 0;
+    size_t part_bytes = 0, cnt_bytes = 0;
+    size_t bytes() const { return part_bytes + cnt_bytes; }
+};
+// Decide whether the launch `plan` runs with a stream-K tail and size it.
+// flags: WSG_FLAG_STREAM_K forces it, WSG_FLAG_NO_STREAM_K forbids it; by
+// default it is used when the last round of tiles would be at most 90% full.
+SkShape plan_stream_k(const GemmPlan &plan, int64_t M, int64_t N, int64_t K, int flags, const DeviceInfo &dev);
+// `sk` null or unused: one workgroup per tile. Otherwise `ws` is a device
+// workspace of at least sk->bytes() bytes, 256-byte aligned.
 int launch_gemm(const LaunchCtx &ctx, const GemmPlan &plan, int64_t M, int64_t N, int64_t K, const void *A,
-                const void *B, const void *bias, float *C, std::string *err);
+                const void *B, const void *bias, float *C, const SkShape *sk, void *ws, std::string *err);
 // One launch over the tiles of `groups` experts (rows sorted by expert,
 // group_rows[e] rows each; B and bias hold one block per expert); `plan` was
 // made for the total row count.
