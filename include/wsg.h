@@ -100,6 +100,28 @@ int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, cons
 int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                       const void *bias, float *C, int stages, const wsg_config *cfg);
 
+/* Bytes of the per-device scratch array of gemm_bias_relu_ex_noalloc: 40 MiB. */
+#define WSG_NOALLOC_SCRATCH_BYTES 41943040
+
+/*
+ * gemm_bias_relu_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same kernels and results as gemm_bias_relu_ex (bit for bit,
+ * same arguments and configuration), but the stream-K workspace is a static
+ * device array of WSG_NOALLOC_SCRATCH_BYTES that every GPU the library runs
+ * on holds until the process ends; no call allocates or frees. A launch whose
+ * stream-K workspace would exceed it returns WSG_EUNSUPPORTED (on a 256-CU
+ * device the built tile shapes need 32 MiB of partial sums, one tile's fp32
+ * accumulators per resident workgroup, and a few KiB of counters;
+ * WSG_FLAG_NO_STREAM_K needs none). The array keeps the last call's contents;
+ * each launch clears the counters it uses, with a kernel. All calls on one
+ * GPU share the array: calls that may overlap on that GPU (on different
+ * streams, or from different threads without ordering) race and must be
+ * serialized by the caller.
+ */
+int gemm_bias_relu_ex_noalloc(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                              const void *bias, float *C, int stages, const wsg_config *cfg);
+
 /* Largest number of experts one grouped launch takes. */
 #define WSG_MAX_GROUPS 64
 

@@ -8,8 +8,8 @@ exceptions. There is no fallback: if libwsg.so is missing or fails to load,
 importing this package raises.
 
 Names follow the C ABI: gemm_bias_relu, gemm_bias_relu_bf16,
-gemm_bias_relu_ex, grouped_gemm_bias_relu_ex, attention_fwd, staged_copy, staged_copy_ex, resolve_config,
-check_device_status, set_stream, get_stream, last_error, version.
+gemm_bias_relu_ex, gemm_bias_relu_ex_noalloc, grouped_gemm_bias_relu_ex, attention_fwd, staged_copy,
+staged_copy_ex, resolve_config, check_device_status, set_stream, get_stream, last_error, version.
 """
 from __future__ import annotations
 
@@ -18,13 +18,13 @@ import os
 
 __all__ = [
     "WsgError", "Config", "lib", "library_path", "EXPORTS",
-    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "attention_fwd",
-    "resolve_config",
+    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "gemm_bias_relu_ex_noalloc",
+    "grouped_gemm_bias_relu_ex", "attention_fwd", "resolve_config",
     "staged_copy", "staged_copy_ex", "check_device_status", "set_wait_stats", "read_wait_stats",
     "set_stream", "get_stream", "status_message",
     "last_error", "version", "WSG_FP32", "WSG_BF16", "WSG_FLAG_GENERAL_PRODUCER", "WSG_FLAG_NONTEMPORAL",
     "WSG_FLAG_HOMOGENEOUS", "WSG_FLAG_DIRECT_COPY", "WSG_FLAG_STREAM_K", "WSG_FLAG_NO_STREAM_K",
-    "WSG_MAX_GROUPS",
+    "WSG_MAX_GROUPS", "WSG_NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +44,7 @@ WSG_FLAG_DIRECT_COPY = 8
 WSG_FLAG_STREAM_K = 16
 WSG_FLAG_NO_STREAM_K = 32
 WSG_MAX_GROUPS = 64
+WSG_NOALLOC_SCRATCH_BYTES = 41943040  # 40 MiB
 WSG_STATUS_TIMEOUT = 1
 WSG_STATUS_COPY = 2
 WSG_STATUS_GEMM = 4
@@ -51,8 +52,8 @@ WSG_STATUS_ATTENTION = 8
 
 # every function include/wsg.h declares
 EXPORTS = (
-    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "grouped_gemm_bias_relu_ex", "attention_fwd",
-    "wsg_gemm_resolve_config", "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
+    "gemm_bias_relu", "gemm_bias_relu_bf16", "gemm_bias_relu_ex", "gemm_bias_relu_ex_noalloc",
+    "grouped_gemm_bias_relu_ex", "attention_fwd", "wsg_gemm_resolve_config", "staged_copy", "staged_copy_ex", "wsg_set_stream", "wsg_get_stream", "wsg_last_error",
     "wsg_check_device_status", "wsg_status_message", "wsg_set_wait_stats", "wsg_read_wait_stats", "wsg_version",
 )
 
@@ -89,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "gemm_bias_relu": ([i64, i64, i64, vp, vp, vp, vp, ci], ci),
         "gemm_bias_relu_bf16": ([i64, i64, i64, vp, vp, vp, vp, ci], ci),
         "gemm_bias_relu_ex": ([ci, i64, i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
+        "gemm_bias_relu_ex_noalloc": ([ci, i64, i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
         "grouped_gemm_bias_relu_ex": ([ci, ci, ctypes.POINTER(i64), i64, i64, vp, vp, vp, vp, ci, cfgp], ci),
         "attention_fwd": ([i64, i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, ci, ci, cfgp], ci),
         "wsg_gemm_resolve_config": ([ci, i64, i64, i64, ci, cfgp, cfgp], ci),
@@ -209,6 +211,24 @@ def gemm_bias_relu_ex(A, B, bias, C=None, stages: int = 4, config=None):
     _use_current_stream()
     _raise_on(lib.gemm_bias_relu_ex(dtype, M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr(), C.data_ptr(),
                                     stages, _config(config)))
+    return C
+
+
+def gemm_bias_relu_ex_noalloc(A, B, bias, C, stages: int = 4, config=None):
+    """gemm_bias_relu_ex without any device allocation, by the library or
+    here: C must be given; the stream-K workspace is the library's static
+    per-device scratch array (calls that may overlap on one GPU race)."""
+    import torch
+    if C is None:
+        raise ValueError("gemm_bias_relu_ex_noalloc allocates nothing: pass the output C")
+    if A.dtype == torch.float32:
+        dtype, ok = WSG_FP32, (torch.float32,)
+    else:
+        dtype, ok = WSG_BF16, _bf16_ok()
+    M, N, K, C = _gemm_operands(A, B, bias, C, ok)
+    _use_current_stream()
+    _raise_on(lib.gemm_bias_relu_ex_noalloc(dtype, M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr(),
+                                            C.data_ptr(), stages, _config(config)))
     return C
 
 

@@ -16,6 +16,11 @@ __device__ unsigned wsg_status_word;
 // Wait statistics (see wsg_read_wait_stats); each GPU holds its own copy.
 __device__ unsigned long long wsg_wait_stats[wsg::kStatWords];
 
+// Stream-K workspace of gemm_bias_relu_ex_noalloc; each GPU holds its own
+// copy until the process ends. Host code never names it in a launch or copy:
+// it uses the device address looked up per device in device_info.
+static __device__ __align__(256) unsigned char scratch[WSG_NOALLOC_SCRATCH_BYTES];
+
 static_assert(wsg::kStatusTimeout == WSG_STATUS_TIMEOUT && wsg::kStatusCopy == WSG_STATUS_COPY &&
                   wsg::kStatusGemm == WSG_STATUS_GEMM && wsg::kStatusAttention == WSG_STATUS_ATTENTION,
               "status bits of the kernels and of the public header");
@@ -61,10 +66,14 @@ int device_info(wsg::DeviceInfo *out) {
         void *st = nullptr;
         e = hipGetSymbolAddress(&st, HIP_SYMBOL(wsg_wait_stats));
         if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+        void *sc = nullptr;
+        e = hipGetSymbolAddress(&sc, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail(WSG_ELAUNCH, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
         d.cu_count = prop.multiProcessorCount;
         d.max_lds = (size_t)lds;
         d.status = static_cast<unsigned *>(p);
         d.stats = static_cast<unsigned long long *>(st);
+        d.scratch = sc;
         d.device = dev;
     }
     *out = d;
@@ -135,8 +144,10 @@ int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, con
     return WSG_OK;
 }
 
+// noalloc: the stream-K workspace is the device's scratch array, never a
+// library allocation; a launch that needs more is rejected
 int gemm_impl(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias, float *C,
-              int stages, const wsg_config *cfg) {
+              int stages, const wsg_config *cfg, bool noalloc = false) {
     int rc = validate_gemm(dtype, M, N, K, A, B, bias, C, stages);
     if (rc != WSG_OK) return rc;
     if (M == 0 || N == 0) return ok();
@@ -151,7 +162,14 @@ int gemm_impl(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
     if (rc != WSG_OK) return fail(rc, err);
     const wsg::SkShape sk = wsg::plan_stream_k(plan, M, N, K, cfg ? cfg->flags : 0, ctx.dev);
     void *ws = nullptr;
-    if (sk.use) {
+    if (sk.use && noalloc) {
+        if (sk.bytes() > (size_t)WSG_NOALLOC_SCRATCH_BYTES)
+            return fail(WSG_EUNSUPPORTED, "stream-K workspace of " + std::to_string(sk.bytes()) +
+                                              " bytes exceeds the " + std::to_string(WSG_NOALLOC_SCRATCH_BYTES) +
+                                              "-byte scratch of gemm_bias_relu_ex_noalloc (WSG_FLAG_NO_STREAM_K "
+                                              "avoids the workspace)");
+        ws = ctx.dev.scratch;
+    } else if (sk.use) {
         rc = sk_workspace(ctx.dev.device, ctx.stream, sk.bytes(), &ws);
         if (rc != WSG_OK) return rc;
     }
@@ -304,6 +322,11 @@ int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, cons
 int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *bias,
                       float *C, int stages, const wsg_config *cfg) {
     return gemm_impl(dtype, M, N, K, A, B, bias, C, stages, cfg);
+}
+
+int gemm_bias_relu_ex_noalloc(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                              const void *bias, float *C, int stages, const wsg_config *cfg) {
+    return gemm_impl(dtype, M, N, K, A, B, bias, C, stages, cfg, true);
 }
 
 int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, int64_t N, int64_t K, const void *A,

@@ -18,6 +18,7 @@ struct DeviceInfo {
     size_t max_lds = 0;  // bytes of LDS one workgroup may allocate
     unsigned *status = nullptr;  // device address of the status word
     unsigned long long *stats = nullptr;  // device address of the wait statistics
+    void *scratch = nullptr;  // device address of this device's allocation-free scratch array
 };
 
 struct LaunchCtx {
