@@ -291,6 +291,22 @@ def run(args):
         except wsg.WsgError as e:
             result["homogeneous_baseline"] = {"error": str(e)}
 
+    if result["config"]["stream_k"] and not args.no_ablation:
+        # the same launch with one workgroup per tile (no stream-K tail), so the
+        # tail's share of the gain over the homogeneous kernel shows
+        ncfg = dict(BM=resolved["BM"], BN=resolved["BN"], BK=resolved["BK"],
+                    producer_waves=resolved["producer_waves"], consumer_waves=resolved["consumer_waves"],
+                    group_k=resolved["group_k"], flags=(args.flags | wsg.WSG_FLAG_NO_STREAM_K) & ~wsg.WSG_FLAG_STREAM_K)
+        dC_n = torch.empty_like(dC)
+        ngemm = lambda: wsg.gemm_bias_relu_ex(dA, dB, dbias, dC_n, stages=stages, config=ncfg)  # noqa: E731
+        for _ in range(args.warmup):
+            ngemm()
+        n_wall, n_kern, _ = time_region(torch, ngemm, args.steps)
+        wsg.check_device_status()
+        result["no_stream_k"] = {"kernel_tflops": round(flops / n_kern / 1e12, 3), "kernel_ms": round(n_kern * 1e3, 4),
+                                 "stream_k_speedup": round(n_kern / g_kern, 4)}
+        del dC_n
+
     if not args.no_vendor:
         # the vendor library (hipBLASLt through torch) on the same operands, for
         # context: relu(addmm) in the input dtype, so its output is bf16 when the

@@ -317,6 +317,9 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 // whoever finishes first) and runs the epilogue. The ring flags carry on
 // across a worker's units: producers stream them back to back.
 // ----------------------------------------------------------------------------
+// Cache policy of the partial-sum stores and loads: sc1, device scope.
+constexpr int kScopeDevice = 16;
+
 struct SkUnit {
     int tile;      // logical tile index (before the tile-row swizzle)
     int kb, ke;    // k-tile range [kb, ke)
@@ -937,24 +940,27 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
             int ln = lane;
             asm volatile("" : "+v"(ln));
             if (un.kind == 2) {
-                // contributor: this worker's partial slot, lane-interleaved
-                // (register r of lane l at r * 64 + l; one lane offset, the
-                // register's in the scalar offset), then count it done
+                // contributor: this worker's partial slot, fragment-major
+                // (fragment q of lane l as 16 bytes at (q * 64 + l) * 16),
+                // stored at device scope (written through to memory, not
+                // left in this XCD's L2); once they have completed, count
+                // the piece done
                 const __amdgpu_buffer_rsrc_t rp =
                     make_rsrc(a.part + ((size_t)w * NCW + cw) * (64 * ACC), 64 * ACC * 4);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][e]), rp, 4 * ln,
-                                                                  ((i * FN + j) * 4 + e) * 256, 0);
-                if (ln == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rp, 16 * ln,
+                                                               (i * FN + j) * 1024, kScopeDevice);
+                wait_vmcnt<0>();
+                if (ln == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 continue;
             }
             if (un.kind == 1) {
-                // owner: wait for the other pieces, add them in piece order
+                // owner: wait for the other pieces, add them in piece order;
+                // device-scope loads see the contributors' device-scope
+                // stores, which completed before their counts
                 const uint32_t need = (uint32_t)(un.npieces - 1);
                 uint32_t spins = 0;
                 while (__builtin_amdgcn_readfirstlane(
@@ -966,18 +972,25 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
                     }
                 }
                 if (!ok) break;
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                asm volatile("" ::: "memory");  // no load of a partial moves above the wait
                 for (int p = 1; p < un.npieces; ++p) {
                     const __amdgpu_buffer_rsrc_t rp =
                         make_rsrc(a.part + ((size_t)(un.first + p) * NCW + cw) * (64 * ACC), 64 * ACC * 4);
+                    // NB fragments in flight at a time: all loads of a batch
+                    // issue before its adds
+                    constexpr int NQ = FM * FN, NB = NQ < 8 ? NQ : 8;
+                    static_assert(NQ % NB == 0, "fragments per batch");
 #pragma unroll
-                    for (int i = 0; i < FM; ++i)
+                    for (int q0 = 0; q0 < NQ; q0 += NB) {
+                        u32x4 t[NB];
 #pragma unroll
-                        for (int j = 0; j < FN; ++j)
+                        for (int q = 0; q < NB; ++q)
+                            t[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, 16 * ln, (q0 + q) * 1024, kScopeDevice);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[i][j][e] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                    rp, 4 * ln, ((i * FN + j) * 4 + e) * 256, 0));
+                        for (int q = 0; q < NB; ++q)
+                            acc[(q0 + q) / FN][(q0 + q) % FN] += __builtin_bit_cast(f32x4, t[q]);
+                    }
                 }
                 if (ln == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
