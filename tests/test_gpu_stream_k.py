@@ -89,6 +89,14 @@ def test_decision(gpu):
     assert not gpu.resolve_config(gpu.WSG_BF16, 3000, 5000, 4096, 2, dict(flags=STREAM_K))["flags"] & STREAM_K
     # K == 0: nothing to split; C = relu(bias)
     assert not _uses_sk(gpu, 300, 520, 0, 2, dict(flags=STREAM_K))
+    # fewer 256 x 128 tiles than CUs but a deep K: the big tile, split along K
+    r = gpu.resolve_config(gpu.WSG_FP32, 1024, 1024, 16384, 2)
+    assert (r["BM"], r["BN"]) == (256, 128) and r["flags"] & STREAM_K
+    # ... unless stream-K is turned off, or K is too short to give every CU 16 k steps
+    r = gpu.resolve_config(gpu.WSG_FP32, 1024, 1024, 16384, 2, dict(flags=NO_STREAM_K))
+    assert (r["BM"], r["BN"]) == (64, 64) and not r["flags"] & STREAM_K
+    r = gpu.resolve_config(gpu.WSG_FP32, 1024, 1024, 1024, 2)
+    assert (r["BM"], r["BN"]) == (64, 64) and not r["flags"] & STREAM_K
 
 
 def test_workspace_reuse_and_growth(gpu):
@@ -148,3 +156,15 @@ def test_full_size_ragged_default(gpu):
     assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
     s = oracle.compare(C1[rows], oracle.gemm_bias_relu_rows(A, B, bias, rows))
     assert oracle.within_tolerance(s, "fp32"), s
+
+
+def test_deep_k_default(gpu):
+    """1024 x 1024 x 16384 by default: 32 tiles of 256 x 128 whose 512 k steps each are shared by every
+    CU; integer inputs exact on rows of every tile row, and repeatable."""
+    M, N, K = 1024, 1024, 16384
+    A, B, bias = int_case(6700, M, N, K)
+    C = run_gemm(gpu, A, B, bias, stages=2)
+    rows = stratified_rows(M, 256, 5)
+    assert np.array_equal(C[rows].astype(np.float64), oracle.gemm_bias_relu_rows(A, B, bias, rows))
+    C2 = run_gemm(gpu, A, B, bias, stages=2, guards=False)
+    assert np.array_equal(C.view(np.uint32), C2.view(np.uint32))

@@ -319,6 +319,9 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 // ----------------------------------------------------------------------------
 // Cache policy of the partial-sum stores and loads: sc1, device scope.
 constexpr int kScopeDevice = 16;
+// Fewest k steps per worker for which a launch with fewer tiles than workers
+// is split by stream-K by default.
+constexpr int64_t kStreamKMinSteps = 16;
 
 struct SkUnit {
     int tile;      // logical tile index (before the tile-row swizzle)
@@ -1380,12 +1383,23 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
                "WSG_FLAG_GENERAL_PRODUCER clear";
         return WSG_EINVAL;
     }
+    // the DMA producer needs 16-byte aligned rows and offsets within 31 bits
+    const int align_elems = 16 / esz;
+    const bool aligned = K % align_elems == 0 && N % align_elems == 0 && ((uintptr_t)A % 16) == 0 &&
+                         ((uintptr_t)B % 16) == 0;
     const bool default_tile = !BM && !BN && !BK;
     if (default_tile) {
         // default tile by problem size: small problems need more workgroups
         const int64_t big = (M + 255) / 256 * ((N + 127) / 128);
         const int64_t mid = (M + 127) / 128 * ((N + 127) / 128);
-        if (big >= (int64_t)dev.cu_count) {
+        // fp32 with fewer 256 x 128 tiles than CUs but a deep K: keep the big
+        // tile and let a stream-K launch split the k steps over every CU
+        // (measured on MI355X: 1024 x 1024 x 16384 117 TFLOP/s against 40 with
+        // 64 x 64 tiles; 2048 x 2048 x 8192 130 against 115 with 128 x 128)
+        const bool deep_k = dtype == WSG_FP32 && !homogeneous && !force_general && aligned &&
+                            !(cfg && (cfg->flags & WSG_FLAG_NO_STREAM_K)) &&
+                            big * ((K + 31) / 32) >= kStreamKMinSteps * (int64_t)dev.cu_count;
+        if (big >= (int64_t)dev.cu_count || deep_k) {
             BM = 256;
             BN = 128;
         } else if (mid >= (int64_t)dev.cu_count / 2) {
@@ -1396,10 +1410,6 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
             BN = 64;
         }
     }
-    // the DMA producer needs 16-byte aligned rows and offsets within 31 bits
-    const int align_elems = 16 / esz;
-    const bool aligned = K % align_elems == 0 && N % align_elems == 0 && ((uintptr_t)A % 16) == 0 &&
-                         ((uintptr_t)B % 16) == 0;
     if (homogeneous && !aligned) {
         *err = "the homogeneous kernel loads by LDS-DMA: K and N must be multiples of " + std::to_string(align_elems) +
                " and A and B 16-byte aligned";
@@ -1528,9 +1538,14 @@ SkShape plan_stream_k(const GemmPlan &plan, int64_t M, int64_t N, int64_t K, int
     const int64_t tiles = plan.tiles_m * plan.tiles_n;
     const int64_t rounds = tiles / workers, rem = tiles % workers;
     if (!(flags & WSG_FLAG_STREAM_K)) {
-        // a tail worth spreading: at least one whole round, and a last round
-        // at most 90% full (480 tiles on 256 CUs: 224 in the last round)
-        if (rounds < 1 || rem == 0 || rem * 10 > workers * 9) return sk;
+        // a tail worth spreading: a last round at most 90% full (480 tiles on
+        // 256 CUs: 224 in the last round) after at least one whole round, or
+        // fewer tiles than workers but enough k steps to give each worker
+        // kStreamKMinSteps of them
+        const int64_t steps = tiles * ((K + v.BK - 1) / v.BK);
+        const bool tail = rounds >= 1 && rem > 0 && rem * 10 <= workers * 9;
+        const bool deep = rounds == 0 && steps >= kStreamKMinSteps * workers;
+        if (!tail && !deep) return sk;
     }
     if (workers * (int64_t)v.BM * v.BN * 4 >= 0x7FFFFFFF) return sk;
     sk.use = true;
