@@ -104,3 +104,40 @@ def test_binding_requires_output(gpu):
     C = torch.full((8, 8), -1.0, device="cuda")
     gpu.gemm_bias_relu_ex_noalloc(A, A, b, C)
     assert torch.equal(C, torch.zeros_like(C))
+
+
+def test_graph_capture_replays(gpu):
+    """The caller this entry point is for: a HIP graph that captures it (counter clearing and the
+    stream-K launch included) is replayed three times, with the program's own eager work and
+    synchronizations between replays; every replay equals the eager result."""
+    import torch
+    M, N, K = 3000, 5000, 4100  # a stream-K tail by default
+    assert gpu.resolve_config(gpu.WSG_FP32, M, N, K, 2)["flags"] & STREAM_K
+    A = synth.uniform_pm1(synth.seed_for(4, "A"), M * K).reshape(M, K)
+    B = synth.uniform_pm1(synth.seed_for(4, "B"), K * N).reshape(K, N)
+    bias = synth.uniform_pm1(synth.seed_for(4, "bias"), N)
+    dA, dB, db = _dev(A, B, bias)
+    C_eager = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    gpu.gemm_bias_relu_ex_noalloc(dA, dB, db, C_eager, stages=2)  # also does the one-time set-up
+    torch.cuda.synchronize()
+    gpu.check_device_status()
+    C = torch.empty_like(C_eager)
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    say("capture gemm_bias_relu_ex_noalloc M=%d N=%d K=%d" % (M, N, K))
+    with torch.cuda.graph(graph, stream=side):
+        gpu.gemm_bias_relu_ex_noalloc(dA, dB, db, C, stages=2)
+    Ai, Bi, bi = int_case(7400, 700, 900, 660)
+    dAi, dBi, dbi = _dev(Ai, Bi, bi)
+    Ci = torch.empty((700, 900), dtype=torch.float32, device="cuda")
+    for i in range(3):
+        C.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        gpu.check_device_status()
+        assert torch.equal(C, C_eager), "replay %d" % i
+        # eager work on the same scratch array between replays
+        gpu.gemm_bias_relu_ex_noalloc(dAi, dBi, dbi, Ci, stages=2, config=dict(flags=STREAM_K))
+        torch.cuda.synchronize()
+        assert np.array_equal(Ci.cpu().numpy().astype(np.float64), oracle.gemm_bias_relu(Ai, Bi, bi))
