@@ -177,7 +177,9 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  * round is split); WSG_FLAG_NO_STREAM_K forbids it. The partial sums and
  * counters live in a device workspace the library allocates on first need
  * per (device, stream) and keeps until the process ends; growing it waits
- * for that stream. A failed wait on another piece sets WSG_STATUS_TIMEOUT.
+ * for that stream, so a launch that would need to allocate or grow it cannot
+ * be captured in a HIP graph (gemm_bias_relu_ex_noalloc can). A failed wait
+ * on another piece sets WSG_STATUS_TIMEOUT.
  */
 
 /*
