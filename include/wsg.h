@@ -165,10 +165,11 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  * Stream-K tail (fp32, wave-specialized LDS-DMA kernels; not from the pages,
  * which launch one workgroup per output tile): when the tiles fill at least
  * one round of the device's resident workgroups and the last round is at most
- * 90% full, or when there are fewer tiles than resident workgroups but at
- * least 16 k steps of BK per workgroup, the launch is a persistent grid of one
- * round. With the default tile, such a deep-K problem also keeps the 256 x 128
- * tile rather than a smaller one. Each workgroup takes
+ * 90% full, or when there are fewer tiles of 256 x 128 or more than resident
+ * workgroups but at least 16 k steps of BK per workgroup, the launch is a
+ * persistent grid of one round. With the default tile, such a deep-K problem
+ * keeps the 256 x 128 tile rather than a smaller one when 128 x 128 tiles
+ * would leave CUs idle or there are at least 64 k steps per CU. Each workgroup takes
  * its whole-tile rounds, then an equal share of the remaining tiles' K steps;
  * a tile split between workgroups is summed in a fixed order (the piece with
  * k = 0 first, then the others by increasing k), so results do not depend on

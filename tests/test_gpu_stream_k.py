@@ -97,6 +97,13 @@ def test_decision(gpu):
     assert (r["BM"], r["BN"]) == (64, 64) and not r["flags"] & STREAM_K
     r = gpu.resolve_config(gpu.WSG_FP32, 1024, 1024, 1024, 2)
     assert (r["BM"], r["BN"]) == (64, 64) and not r["flags"] & STREAM_K
+    # ... or when 256 tiles of 128 x 128 fill the chip and K is not very deep
+    r = gpu.resolve_config(gpu.WSG_FP32, 2048, 2048, 1024, 2)
+    assert (r["BM"], r["BN"]) == (128, 128) and not r["flags"] & STREAM_K
+    r = gpu.resolve_config(gpu.WSG_FP32, 2048, 2048, 8192, 2)
+    assert (r["BM"], r["BN"]) == (256, 128) and r["flags"] & STREAM_K
+    # small tiles chosen explicitly with fewer tiles than workers: not split by default
+    assert not _uses_sk(gpu, 1024, 1024, 16384, 2, dict(BM=128, BN=128, BK=32))
 
 
 def test_workspace_reuse_and_growth(gpu):

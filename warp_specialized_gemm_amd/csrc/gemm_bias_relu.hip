@@ -1393,12 +1393,16 @@ int plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const v
         const int64_t big = (M + 255) / 256 * ((N + 127) / 128);
         const int64_t mid = (M + 127) / 128 * ((N + 127) / 128);
         // fp32 with fewer 256 x 128 tiles than CUs but a deep K: keep the big
-        // tile and let a stream-K launch split the k steps over every CU
-        // (measured on MI355X: 1024 x 1024 x 16384 117 TFLOP/s against 40 with
-        // 64 x 64 tiles; 2048 x 2048 x 8192 130 against 115 with 128 x 128)
+        // tile and let a stream-K launch split the k steps over every CU, if
+        // 128 x 128 tiles would leave CUs idle or K is very deep (measured on
+        // MI355X, TFLOP/s, stream-K 256 x 128 against the smaller default:
+        // 1024 x 1024 x 16384 117 / 40; 1024 x 2048 x 2048 91 / 58;
+        // 2048 x 2048 x 8192 130 / 117; but 2048 x 2048 x 1024 98 / 105 and
+        // 2048^3 115 / 113, where 256 tiles of 128 x 128 fill the chip)
+        const int64_t steps_per_cu = big * ((K + 31) / 32) / dev.cu_count;
         const bool deep_k = dtype == WSG_FP32 && !homogeneous && !force_general && aligned &&
-                            !(cfg && (cfg->flags & WSG_FLAG_NO_STREAM_K)) &&
-                            big * ((K + 31) / 32) >= kStreamKMinSteps * (int64_t)dev.cu_count;
+                            !(cfg && (cfg->flags & WSG_FLAG_NO_STREAM_K)) && steps_per_cu >= kStreamKMinSteps &&
+                            (mid < (int64_t)dev.cu_count || steps_per_cu >= 4 * kStreamKMinSteps);
         if (big >= (int64_t)dev.cu_count || deep_k) {
             BM = 256;
             BN = 128;
@@ -1540,11 +1544,13 @@ SkShape plan_stream_k(const GemmPlan &plan, int64_t M, int64_t N, int64_t K, int
     if (!(flags & WSG_FLAG_STREAM_K)) {
         // a tail worth spreading: a last round at most 90% full (480 tiles on
         // 256 CUs: 224 in the last round) after at least one whole round, or
-        // fewer tiles than workers but enough k steps to give each worker
-        // kStreamKMinSteps of them
+        // fewer 256 x 128 (or larger) tiles than workers but enough k steps
+        // to give each worker kStreamKMinSteps of them; smaller tiles were
+        // chosen to fill the chip (split 128 x 128 tiles ran slower than
+        // whole ones: 88 against 105 TFLOP/s on 2048 x 2048 x 1024)
         const int64_t steps = tiles * ((K + v.BK - 1) / v.BK);
         const bool tail = rounds >= 1 && rem > 0 && rem * 10 <= workers * 9;
-        const bool deep = rounds == 0 && steps >= kStreamKMinSteps * workers;
+        const bool deep = rounds == 0 && v.BM * v.BN >= 256 * 128 && steps >= kStreamKMinSteps * workers;
         if (!tail && !deep) return sk;
     }
     if (workers * (int64_t)v.BM * v.BN * 4 >= 0x7FFFFFFF) return sk;
