@@ -100,8 +100,8 @@ int gemm_bias_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, cons
 int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                       const void *bias, float *C, int stages, const wsg_config *cfg);
 
-/* Bytes of the per-device scratch array of gemm_bias_relu_ex_noalloc: 40 MiB. */
-#define WSG_NOALLOC_SCRATCH_BYTES 41943040
+/* Bytes of the per-device scratch array of gemm_bias_relu_ex_noalloc: 72 MiB. */
+#define WSG_NOALLOC_SCRATCH_BYTES 75497472
 
 /*
  * gemm_bias_relu_ex for callers that cannot allocate device memory: code
@@ -111,7 +111,7 @@ int gemm_bias_relu_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
  * device array of WSG_NOALLOC_SCRATCH_BYTES that every GPU the library runs
  * on holds until the process ends; no call allocates or frees. A launch whose
  * stream-K workspace would exceed it returns WSG_EUNSUPPORTED (on a 256-CU
- * device the built tile shapes need 32 MiB of partial sums, one tile's fp32
+ * device the built tile shapes need 64 MiB of partial sums, two tiles' fp32
  * accumulators per resident workgroup, and a few KiB of counters;
  * WSG_FLAG_NO_STREAM_K needs none). The array keeps the last call's contents;
  * each launch clears the counters it uses, with a kernel. All calls on one
@@ -171,16 +171,16 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  * keeps the 256 x 128 tile rather than a smaller one when 128 x 128 tiles
  * would leave CUs idle or there are at least 64 k steps per CU. Each workgroup takes
  * its whole-tile rounds, then an equal share of the remaining tiles' K steps;
- * a tile split between workgroups is summed in a fixed order (the piece with
- * k = 0 first, then the others by increasing k), so results do not depend on
- * timing but differ in rounding from the one-workgroup-per-tile launch.
+ * a tile split between workgroups is summed in a fixed order (its pieces by
+ * increasing k, added by whichever workgroup finishes the last piece; no
+ * workgroup waits for another), so results do not depend on timing but differ
+ * in rounding from the one-workgroup-per-tile launch.
  * WSG_FLAG_STREAM_K forces the split (with no ragged round, the last full
  * round is split); WSG_FLAG_NO_STREAM_K forbids it. The partial sums and
  * counters live in a device workspace the library allocates on first need
  * per (device, stream) and keeps until the process ends; growing it waits
  * for that stream, so a launch that would need to allocate or grow it cannot
- * be captured in a HIP graph (gemm_bias_relu_ex_noalloc can). A failed wait
- * on another piece sets WSG_STATUS_TIMEOUT.
+ * be captured in a HIP graph (gemm_bias_relu_ex_noalloc can).
  */
 
 /*

@@ -44,7 +44,7 @@ WSG_FLAG_DIRECT_COPY = 8
 WSG_FLAG_STREAM_K = 16
 WSG_FLAG_NO_STREAM_K = 32
 WSG_MAX_GROUPS = 64
-WSG_NOALLOC_SCRATCH_BYTES = 41943040  # 40 MiB
+WSG_NOALLOC_SCRATCH_BYTES = 75497472  # 72 MiB
 WSG_STATUS_TIMEOUT = 1
 WSG_STATUS_COPY = 2
 WSG_STATUS_GEMM = 4

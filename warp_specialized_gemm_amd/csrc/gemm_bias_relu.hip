@@ -304,18 +304,19 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
 // Stream-K tail (fp32 kernels built with SK). When the output tiles do not
 // fill a whole number of rounds of the persistent grid (`workers` workgroups,
 // as many as the device holds at once), the last, partial round would leave
-// CUs idle: 480 tiles of
-// 256 x 128 on 256 CUs run as a full round and a round of 224. Instead, each
-// worker w first computes data-parallel tiles w, w + workers, ... (dp_tiles
-// of them in all, whole rounds only), then an equal contiguous share of the
-// remaining sk_tiles x T k-tile steps (tile-major, k ascending). A share is
-// shorter than a tile, so it covers at most two tiles: the end of one (a
-// "contributor" piece) and the start of the next (its "owner" piece, k from
-// 0). A contributor stores its fp32 accumulators in the worker's partial
-// slot, then counts itself done on the tile; the owner waits for the tile's
-// other pieces, adds their partials in piece order (so the sum order is fixed
-// whoever finishes first) and runs the epilogue. The ring flags carry on
-// across a worker's units: producers stream them back to back.
+// CUs idle: 480 tiles of 256 x 128 on 256 CUs run as a full round and a round
+// of 224. Instead, each worker w first computes data-parallel tiles w,
+// w + workers, ... (dp_tiles of them in all, whole rounds only), then an equal
+// contiguous share of the remaining sk_tiles x T k-tile steps (tile-major, k
+// ascending). A share is at most one tile long, so it holds at most two
+// pieces: the end of one tile and the start of the next, each stored in a
+// partial slot of its own (2 w and 2 w + 1). Every piece of a split tile is
+// stored, then counted on the tile's counter (per consumer wave); the wave
+// whose count completes the tile reads all of its pieces back in piece order
+// (so the sum order is fixed whoever finishes last) and runs the epilogue.
+// No workgroup ever waits for another, so the launch needs no co-residency.
+// The ring flags carry on across a worker's units: producers stream them back
+// to back.
 // ----------------------------------------------------------------------------
 // Cache policy of the partial-sum stores and loads: sc1, device scope.
 constexpr int kScopeDevice = 16;
@@ -326,9 +327,10 @@ constexpr int64_t kStreamKMinSteps = 16;
 struct SkUnit {
     int tile;      // logical tile index (before the tile-row swizzle)
     int kb, ke;    // k-tile range [kb, ke)
-    int kind;      // 0: the whole tile; 1: owner piece; 2: contributor piece
-    int sk_tile;   // index among the stream-K tiles (kinds 1 and 2)
-    int first, npieces;  // worker of the tile's first piece, pieces of the tile
+    int sk_tile;   // index among the stream-K tiles (split tiles only)
+    int first, npieces;  // worker of the tile's first piece, pieces of the tile (1: whole)
+    int slot;      // partial slot of this piece
+    int first_slot;  // partial slot of the tile's first piece (the others': 2 (first + p))
 };
 
 // Worker whose share of the Z stream-K steps holds step i: shares are
@@ -340,19 +342,20 @@ __device__ __forceinline__ bool sk_unit(const GemmArgs &a, int T, int w, int u, 
     const int G = a.workers;
     const int rounds = a.dp_tiles / G;
     if (u < rounds) {
-        out = SkUnit{u * G + w, 0, T, 0, -1, w, 1};
+        out = SkUnit{u * G + w, 0, T, -1, w, 1, -1, -1};
         return true;
     }
     int idx = u - rounds;
     // with fewer steps than workers only the first Z workers take one each:
     // every share is then non-empty, so the workers between a tile's first
-    // and last piece all hold a piece of it
+    // and last piece all hold a piece of it; a piece other than a tile's
+    // first starts its worker's share, so it sits in that worker's slot 0
     const int64_t Z = (int64_t)a.sk_tiles * T;
     const int Gs = (int)min((int64_t)G, Z);
     if (w >= Gs) return false;
     int64_t i = (int64_t)w * Z / Gs;
     const int64_t e = (int64_t)(w + 1) * Z / Gs;
-    while (i < e) {
+    for (int piece = 0; i < e; ++piece) {
         const int64_t tau = i / T;
         const int kb = (int)(i - tau * T);
         const int ke = (int)min((int64_t)T, e - tau * T);
@@ -364,7 +367,8 @@ __device__ __forceinline__ bool sk_unit(const GemmArgs &a, int T, int w, int u, 
             out.sk_tile = (int)tau;
             out.first = wf;
             out.npieces = wl - wf + 1;
-            out.kind = out.npieces == 1 ? 0 : (kb == 0 ? 1 : 2);
+            out.slot = 2 * w + piece;
+            out.first_slot = 2 * wf + ((int64_t)wf * Z / Gs == tau * T ? 0 : 1);
             return true;
         }
         --idx;
@@ -936,20 +940,21 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
             if (!ok) break;
             int utm, utn;
             swizzle_tile<kGroupRows>(un.tile, a.tiles_m, a.tiles_n, utm, utn);
-            unsigned *cnt = a.cnt + (size_t)un.sk_tile * NCW + cw;
             // The lane index through an empty asm: addresses derived from it
             // are formed here, not hoisted out of the unit loop where they
             // would stay live (and spill) through the K loop.
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            if (un.kind == 2) {
-                // contributor: this worker's partial slot, fragment-major
-                // (fragment q of lane l as 16 bytes at (q * 64 + l) * 16),
-                // stored at device scope (written through to memory, not
-                // left in this XCD's L2); once they have completed, count
-                // the piece done
+            if (un.npieces > 1) {
+                // a piece: store it in its partial slot, fragment-major
+                // (fragment q of lane l as 16 bytes at (q * 64 + l) * 16), at
+                // device scope (written through to memory, not left in this
+                // XCD's L2); once the stores have completed, count it on the
+                // tile. The wave whose count completes the tile adds every
+                // piece back in piece order, reading at device scope, and
+                // runs the epilogue; the others go on to their next unit.
                 const __amdgpu_buffer_rsrc_t rp =
-                    make_rsrc(a.part + ((size_t)w * NCW + cw) * (64 * ACC), 64 * ACC * 4);
+                    make_rsrc(a.part + ((size_t)un.slot * NCW + cw) * (64 * ACC), 64 * ACC * 4);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -957,28 +962,19 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rp, 16 * ln,
                                                                (i * FN + j) * 1024, kScopeDevice);
                 wait_vmcnt<0>();
-                if (ln == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                continue;
-            }
-            if (un.kind == 1) {
-                // owner: wait for the other pieces, add them in piece order;
-                // device-scope loads see the contributors' device-scope
-                // stores, which completed before their counts
-                const uint32_t need = (uint32_t)(un.npieces - 1);
-                uint32_t spins = 0;
-                while (__builtin_amdgcn_readfirstlane(
-                           __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins > kSpinLimit) {
-                        ok = false;
-                        break;
-                    }
-                }
-                if (!ok) break;
-                asm volatile("" ::: "memory");  // no load of a partial moves above the wait
-                for (int p = 1; p < un.npieces; ++p) {
-                    const __amdgpu_buffer_rsrc_t rp =
-                        make_rsrc(a.part + ((size_t)(un.first + p) * NCW + cw) * (64 * ACC), 64 * ACC * 4);
+                unsigned *cnt = a.cnt + (size_t)un.sk_tile * NCW + cw;
+                uint32_t before = 0;
+                if (ln == 0) before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (__builtin_amdgcn_readfirstlane(before) + 1 != (uint32_t)un.npieces) continue;
+                asm volatile("" ::: "memory");  // no load of a piece moves above the count
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int p = 0; p < un.npieces; ++p) {
+                    const int slot = p == 0 ? un.first_slot : 2 * (un.first + p);
+                    const __amdgpu_buffer_rsrc_t rq =
+                        make_rsrc(a.part + ((size_t)slot * NCW + cw) * (64 * ACC), 64 * ACC * 4);
                     // NB fragments in flight at a time: all loads of a batch
                     // issue before its adds
                     constexpr int NQ = FM * FN, NB = NQ < 8 ? NQ : 8;
@@ -988,14 +984,13 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_f32_kernel(typename
                         u32x4 t[NB];
 #pragma unroll
                         for (int q = 0; q < NB; ++q)
-                            t[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, 16 * ln, (q0 + q) * 1024, kScopeDevice);
+                            t[q] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * ln, (q0 + q) * 1024, kScopeDevice);
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int q = 0; q < NB; ++q)
                             acc[(q0 + q) / FN][(q0 + q) % FN] += __builtin_bit_cast(f32x4, t[q]);
                     }
                 }
-                if (ln == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             // epilogue through a buffer resource at the tile's origin (as in
             // the single-fragment bf16 kernels): one lane offset, each store's
@@ -1553,12 +1548,12 @@ SkShape plan_stream_k(const GemmPlan &plan, int64_t M, int64_t N, int64_t K, int
         const bool deep = rounds == 0 && v.BM * v.BN >= 256 * 128 && steps >= kStreamKMinSteps * workers;
         if (!tail && !deep) return sk;
     }
-    if (workers * (int64_t)v.BM * v.BN * 4 >= 0x7FFFFFFF) return sk;
+    if (2 * workers * (int64_t)v.BM * v.BN * 4 >= 0x7FFFFFFF) return sk;
     sk.use = true;
     sk.workers = (int)workers;
     sk.dp_tiles = rem == 0 ? (rounds - 1) * workers : rounds * workers;  // forced with no tail: split the last round
     sk.sk_tiles = tiles - sk.dp_tiles;
-    sk.part_bytes = (size_t)workers * v.BM * v.BN * 4;
+    sk.part_bytes = (size_t)2 * workers * v.BM * v.BN * 4;  // two pieces per worker
     sk.cnt_bytes = ((size_t)sk.sk_tiles * v.CWM * v.CWN * 4 + 255) / 256 * 256;
     return sk;
 }
