@@ -127,7 +127,11 @@ def time_region(torch, fn, steps: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    LAST_MEDIAN[0] = sorted(per)[len(per) // 2]
     return wall, sum(per) / len(per), min(per)
+
+
+LAST_MEDIAN = [0.0]  # median per-launch kernel time of the latest time_region call
 
 
 def cpu_model() -> str:
@@ -230,6 +234,7 @@ def run(args):
 
     log("timing %d steps" % args.steps)
     g_wall, g_kern, g_min = time_region(torch, gemm, args.steps)
+    g_med = LAST_MEDIAN[0]
     wsg.check_device_status()
     flops = 2.0 * M * N * K
     gemm_tflops = flops * args.steps / g_wall / 1e12
@@ -254,6 +259,7 @@ def run(args):
             "group_k": resolved["group_k"], "homogeneous": bool(resolved["flags"] & wsg.WSG_FLAG_HOMOGENEOUS),
             "stream_k": bool(resolved["flags"] & wsg.WSG_FLAG_STREAM_K),
             "input": "uniform[-1,1) splitmix64" if dtype == "fp32" else "N(0,1)*0.1 rounded to bf16",
+            "seeds": {t: synth.seed_for(args.workload, t) for t in ("A", "B", "bias")},
         },
     }
     peak = PEAK_TFLOPS[dtype]
@@ -262,7 +268,8 @@ def run(args):
                                                                          ("BM", "BN", "BK"))), "gemm")
     result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                           "frac": round(achieved / peak, 4), "traffic": traffic,
-                          "kernel_ms": round(g_kern * 1e3, 4), "kernel_ms_min": round(g_min * 1e3, 4)}
+                          "kernel_ms": round(g_kern * 1e3, 4), "kernel_ms_min": round(g_min * 1e3, 4),
+                          "kernel_ms_median": round(g_med * 1e3, 4)}
     step_s = g_wall / args.steps
 
     if not args.homogeneous and not args.no_ablation:
@@ -331,6 +338,7 @@ def run(args):
 
     if copy_src is not None:
         c_wall, c_kern, c_min = time_region(torch, copy, args.steps)
+        c_med = LAST_MEDIAN[0]
         wsg.check_device_status()
         nbytes = cw["bytes"]
         moved = 2.0 * nbytes
@@ -343,7 +351,9 @@ def run(args):
         result["copy_roofline"] = {"bound": "hbm", "achieved": round(c_ach, 1), "peak": PEAK_HBM_GBS,
                                    "unit": "GB/s", "frac": round(c_ach / PEAK_HBM_GBS, 4),
                                    "traffic": measured_traffic("copy_1GiB_64KiB", "copy"),
-                                   "kernel_ms": round(c_kern * 1e3, 4), "kernel_ms_min": round(c_min * 1e3, 4)}
+                                   "kernel_ms": round(c_kern * 1e3, 4), "kernel_ms_min": round(c_min * 1e3, 4),
+                                   "kernel_ms_median": round(c_med * 1e3, 4)}
+        result["copy"]["seed"] = synth.seed_for(2, "src")
         step_s += c_wall / args.steps
         # torch's own device copy of the same buffers, timed the same way: what
         # a plain (unstaged) copy kernel reaches on this device
