@@ -35,6 +35,32 @@ def test_gemm_wait_counts_match_protocol(gpu):
     assert gpu.read_wait_stats()["gemm_consumer_full"]["waits"] == 0
 
 
+@pytest.mark.parametrize("M,N,K,flags", [(700, 900, 660, 16), (1024, 1024, 16384, 0)])
+def test_stream_k_wait_counts_match_protocol(gpu, M, N, K, flags):
+    """A stream-K launch (forced, or by default for a deep K) walks every k tile of every output tile
+    through the ring exactly once, whatever the split: one full wait per consumer wave and one empty
+    wait per producer wave for each of them, as the one-workgroup-per-tile launch."""
+    import torch
+    cfg = dict(BM=256, BN=128, BK=32, producer_waves=4, consumer_waves=4, flags=flags)
+    assert gpu.resolve_config(gpu.WSG_FP32, M, N, K, 2, cfg)["flags"] & 16  # WSG_FLAG_STREAM_K
+    A = torch.from_numpy(synth.uniform_pm1(4, M * K).reshape(M, K)).cuda()
+    B = torch.from_numpy(synth.uniform_pm1(5, K * N).reshape(K, N)).cuda()
+    b = torch.from_numpy(synth.uniform_pm1(6, N)).cuda()
+    gpu.read_wait_stats()  # clear
+    gpu.set_wait_stats(True)
+    try:
+        say("stream-K wait stats %dx%dx%d %s" % (M, N, K, cfg))
+        gpu.gemm_bias_relu_ex(A, B, b, stages=2, config=cfg)
+        st = gpu.read_wait_stats()
+    finally:
+        gpu.set_wait_stats(False)
+    steps = -(-M // 256) * -(-N // 128) * -(-K // 32)
+    assert st["gemm_consumer_full"]["waits"] == 4 * steps
+    assert st["gemm_producer_empty"]["waits"] == 4 * steps
+    for k in ("gemm_consumer_full", "gemm_producer_empty"):
+        assert st[k]["blocked"] <= st[k]["waits"]
+
+
 def test_copy_wait_counts_match_protocol(gpu):
     import torch
     tile = 16384
