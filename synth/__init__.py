@@ -136,13 +136,15 @@ def splitmix64(seed: int, n: int, start: int = 0) -> np.ndarray:
     """
     out = np.empty(int(n), dtype=np.uint64)
     s = np.uint64(int(seed) & 0xFFFFFFFFFFFFFFFF)
-    with np.errstate(over="ignore"):
-        for lo in range(0, int(n), _CHUNK):
-            hi = min(int(n), lo + _CHUNK)
+
+    def work(lo, hi):
+        with np.errstate(over="ignore"):
             z = np.arange(start + lo + 1, start + hi + 1, dtype=np.uint64)
             z *= GOLDEN
             z += s
             out[lo:hi] = _mix(z)
+
+    _parallel_chunks(int(n), _CHUNK, work)
     return out
 
 
@@ -193,12 +195,26 @@ def normal_bf16_bits(seed: int, n: int, scale: float = 0.1) -> np.ndarray:
 
 
 def small_int_f32(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
-    """Integer-valued fp32, uniform on {lo, ..., hi}."""
-    x = splitmix64(seed, n)
+    """Integer-valued fp32, uniform on {lo, ..., hi}: lo + ((x >> 32) mod (hi - lo + 1))."""
+    out = np.empty(int(n), dtype=np.float32)
     span = np.uint64(hi - lo + 1)
-    return ((x >> np.uint64(32)) % span).astype(np.int64).astype(np.float32) + np.float32(lo)
+
+    def work(a, b):
+        x = splitmix64(seed, b - a, start=a)
+        out[a:b] = ((x >> np.uint64(32)) % span).astype(np.int64).astype(np.float32) + np.float32(lo)
+
+    _parallel_chunks(int(n), _CHUNK, work)
+    return out
 
 
 def small_int_bf16_bits(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     """Integer-valued bf16 bits, uniform on {lo, ..., hi} (|values| <= 256 are exact)."""
-    return f32_to_bf16_bits_rne(small_int_f32(seed, n, lo, hi))
+    out = np.empty(int(n), dtype=np.uint16)
+
+    def work(a, b):
+        x = splitmix64(seed, b - a, start=a)
+        v = ((x >> np.uint64(32)) % np.uint64(hi - lo + 1)).astype(np.int64).astype(np.float32) + np.float32(lo)
+        out[a:b] = f32_to_bf16_bits_rne(v)
+
+    _parallel_chunks(int(n), _CHUNK, work)
+    return out
