@@ -6,15 +6,20 @@ bytes; the planner switches to kernels with 64-bit addressing where a tile's
 rows would span more. Each GEMM case sits on one side of such a threshold,
 with integer inputs whose sums stay below 2^24, so the result must match the
 oracle bit for bit on rows of every tile row. The copy moves more than 4 GiB,
-so its byte offsets pass 2^31 and 2^32. The ring cases run the deepest ring
-that fits in LDS and check that one slot more is refused.
+so its byte offsets pass 2^31 and 2^32; attention and the grouped GEMM take
+operands past 2^31 bytes, whose per-head and per-expert bases are 64-bit. The
+ring cases run the deepest ring that fits in LDS and check that one slot more
+is refused.
 """
+import math
+
 import numpy as np
 import pytest
 
 import oracle
 import synth
 from conftest import say, stratified_rows
+from oracle import attention as att
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +188,69 @@ def test_gemm_deepest_ring(gpu, dtype):
     with pytest.raises(gpu.WsgError) as e:
         gpu.gemm_bias_relu_ex(*dev, stages=deepest + 1, config=config)
     assert e.value.code == gpu.WSG_EUNSUPPORTED
+
+
+def _pooled(pool, count):
+    """Blocks 0 .. count - 1 where block i is pool[i mod len(pool)], built on the GPU."""
+    import torch
+    d = torch.from_numpy(np.ascontiguousarray(pool).view(np.int16)).cuda()
+    return d.index_select(0, torch.arange(count, device="cuda") % d.shape[0])
+
+
+def test_attention_past_2_gib(gpu):
+    """2 x 4100 heads of 1024 queries and keys, head dimension 128: Q, K and V
+    pass 2^31 bytes at head 8192, O (fp32) at head 4096 and 2^32 bytes at
+    head 8192. Head i of Q, K and V repeats seeded pools of 61, 59 and 53
+    heads; none of those periods divides 4096 or 8192, so a head read from
+    or written to a wrapped offset would not match the oracle."""
+    import torch
+    Bn, H, S, D = 2, 4100, 1024, 128
+    heads = Bn * H
+    pools = [synth.normal_bf16_bits(7700 + i, p * S * D, scale=1.0).reshape(p, S, D)
+             for i, p in enumerate((61, 59, 53))]
+    dQ, dK, dV = (_pooled(p, heads).view(Bn, H, S, D) for p in pools)
+    dO = torch.empty((Bn, H, S, D), dtype=torch.float32, device="cuda")
+    flat_heads = [0, 4095, 4096, 4100, 8191, 8192, heads - 1]
+    rows = np.array([0, 223, 224, 611, S - 1])
+    scale = 1.0 / math.sqrt(D)
+    for causal in (False, True):
+        dO.fill_(float("nan"))
+        say("attention %s causal=%s default launch" % ((Bn, H, S, D), causal))
+        gpu.attention_fwd(dQ, dK, dV, dO, causal=causal)
+        gpu.check_device_status()
+        assert not bool(torch.isnan(dO).any()), "an output element was not written"
+        got, ref = [], []
+        for f in flat_heads:
+            got.append(dO[f // H, f % H, torch.from_numpy(rows).cuda()].cpu().numpy())
+            q, k, v = (p[f % p.shape[0]][None, None] for p in pools)
+            ref.append(att.attention_rows(q, k, v, scale, causal, 0, 0, rows))
+        s = oracle.compare(np.concatenate(got), np.concatenate(ref))
+        assert oracle.within_tolerance(s, "bf16"), (causal, s)
+    del dQ, dK, dV, dO
+    _free()
+
+
+def test_grouped_weights_past_2_gib(gpu):
+    """16 experts of 8192 x 8200 bf16 weights (2.0 GiB in all; the last
+    expert's block crosses 2^31 bytes), uneven row counts with an empty
+    expert, integer inputs: rows of every expert bit-exact."""
+    import torch
+    E, K, N = 16, 8192, 8200
+    group_rows = [37, 0, 300, 5, 256, 1, 90, 257, 12, 64, 3, 128, 40, 7, 200, 33]
+    M = sum(group_rows)
+    A = synth.small_int_bf16_bits(7801, M * K, -2, 2).reshape(M, K)
+    B = synth.small_int_bf16_bits(7802, E * K * N, -2, 2).reshape(E, K, N)
+    bias = synth.small_int_bf16_bits(7803, E * N, -8, 8).reshape(E, N)
+    dA, dB, db = (torch.from_numpy(x.view(np.int16)).cuda() for x in (A, B, bias))
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    say("grouped gemm bf16 experts=%d K=%d N=%d rows=%d default launch" % (E, K, N, M))
+    gpu.grouped_gemm_bias_relu_ex(dA, dB, db, group_rows, dC)
+    gpu.check_device_status()
+    assert not bool(torch.isnan(dC).any()), "an output element was not written"
+    starts = np.cumsum([0] + group_rows[:-1])
+    rows = np.unique(np.concatenate([[s, s + r // 2, s + r - 1] for s, r in zip(starts, group_rows) if r > 0]))
+    got = dC[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del dA, dB, db, dC
+    _free()
+    want = oracle.grouped_gemm_bias_relu_rows(A, B, bias, group_rows, rows)
+    assert np.array_equal(got.astype(np.float64), want)
