@@ -195,7 +195,9 @@ int grouped_gemm_bias_relu_ex(int dtype, int groups, const int64_t *group_rows, 
  *           patterns, dense row-major, 16-byte aligned.
  *   O       batch x heads x Sq x D fp32, 4-byte aligned, not overlapping the
  *           inputs.
- *   D       64 or 128 (else WSG_EUNSUPPORTED); sizes >= 0; scale finite.
+ *   D       64 or 128 (else WSG_EUNSUPPORTED); sizes >= 0.
+ *   scale   finite and at least 2^-126 (positive and normal), else
+ *           WSG_EINVAL: each row's maximum is taken before scaling.
  *   stages  ring slots of 64 keys (K and V tiles, 32 KiB per slot for
  *           D = 128): 1 .. 4 for D = 128, 1 .. 9 for D = 64.
  *   cfg     may be NULL; cfg->producer_waves (1, 2 or 4; 0 = default) and

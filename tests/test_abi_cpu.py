@@ -110,6 +110,10 @@ def test_grouped_and_attention_arguments_rejected_before_any_device_call(wsg):
     assert a(1, 1, 4, 4, 96, Q, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EUNSUPPORTED
     assert a(1, 1, 4, 4, 128, Q, K, V, O, float("nan"), 0, 2, None) == wsg.WSG_EINVAL
     assert a(1, 1, 4, 4, 128, Q, K, V, O, float("inf"), 0, 2, None) == wsg.WSG_EINVAL
+    # the scale must be positive and normal: zero, negative and subnormal scales are refused
+    for bad in (0.0, -0.0, -1.0, 1e-40, -float("inf")):
+        assert a(1, 1, 4, 4, 128, Q, K, V, O, bad, 0, 2, None) == wsg.WSG_EINVAL, bad
+    assert "scale" in wsg.last_error()
     assert a(1, 1, 4, 4, 128, Q, K, V, O, 1.0, 0, 0, None) == wsg.WSG_EINVAL
     assert a(1, 1, 4, 4, 128, None, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EINVAL
     assert a(1, 1, 4, 4, 128, Q + 2, K, V, O, 1.0, 0, 2, None) == wsg.WSG_EINVAL  # Q not 16-byte aligned

@@ -273,7 +273,7 @@ def grouped_gemm_bias_relu_ex(A, B, bias, group_rows, C=None, stages: int = 4, c
 def attention_fwd(Q, K, V, O=None, scale=None, causal: bool = False, stages: int = 2, config=None):
     """O = softmax(scale * Q K^T [causal]) V; Q (batch, heads, Sq, D), K and V
     (batch, heads, Skv, D) as bf16 tensors or their 16-bit patterns; fp32 O.
-    scale defaults to 1 / sqrt(D)."""
+    scale defaults to 1 / sqrt(D); it must be finite and at least 2^-126."""
     import math
     import torch
     ok = _bf16_ok()

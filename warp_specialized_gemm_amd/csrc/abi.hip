@@ -211,8 +211,11 @@ int attention_impl(int64_t batch, int64_t heads, int64_t Sq, int64_t Skv, int64_
                    const wsg_config *cfg) {
     if (batch < 0 || heads < 0 || Sq < 0 || Skv < 0 || D < 0) return fail(WSG_EINVAL, "negative dimension");
     if (stages < 1) return fail(WSG_EINVAL, "stages must be >= 1");
-    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-        return fail(WSG_EINVAL, "scale must be finite");
+    // the kernel takes each row's maximum before scaling and marks hidden
+    // keys with -inf, so the scale must be positive; at least 2^-126 so that
+    // scale * log2(e) is a normal float, never flushed to zero
+    if (!(scale >= 0x1p-126f) || scale == __builtin_inff())
+        return fail(WSG_EINVAL, "scale must be finite and at least 2^-126");
     if (D != 64 && D != 128) return fail(WSG_EUNSUPPORTED, "head dimension must be 64 or 128");
     if (batch > kMaxDim || heads > kMaxDim || Sq > kMaxDim || Skv > kMaxDim)
         return fail(WSG_EUNSUPPORTED, "dimension above 2^31 - 1");
