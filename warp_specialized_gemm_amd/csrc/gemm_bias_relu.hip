@@ -739,6 +739,29 @@ __device__ __forceinline__ bool consume_lean(int T, int S, unsigned char *ring, 
     return ok;
 }
 
+// A consumer wave whose part of the output tile lies wholly past M or N (the
+// last row tile of an expert in a grouped launch, ragged shapes) has nothing
+// to compute, but the producers count on its release of every slot. It waits
+// for each tile to be published before it releases it, so its arrival falls
+// in the same phase of the empty flag as its siblings'. Its SIMD's other
+// consumer meanwhile has the matrix unit to itself (measured on MI355X, the
+// bf16 expert layer of 8 experts, 8192 routed rows, K 4096, N 14336, where 4
+// experts end in a row tile of at most 128 rows: +2%, bit-identical).
+template <int P, typename Flags>
+__device__ __forceinline__ bool release_only(int T, int S, const Flags &fl, unsigned *status, WaitTally &tally) {
+    int cs = 0;
+    uint32_t lap = 0;
+    for (int t = 0; t < T; ++t) {
+        if (!fl.template wait_full<P>(cs, lap & 1u, status, kStatusGemm, tally)) return false;
+        fl.arrive_empty(cs);
+        if (++cs == S) {
+            cs = 0;
+            ++lap;
+        }
+    }
+    return true;
+}
+
 // ----------------------------------------------------------------------------
 // Homogeneous K loop, the baseline that specialization is measured against
 // (pwwt.cn article, section 1.1: every thread loads the next tile into shared
@@ -1165,6 +1188,12 @@ __global__ void __launch_bounds__((P + CWM * CWN) * 64) gemm_bf16_kernel(typenam
         static_assert(DMA, "the homogeneous loop loads by LDS-DMA");
         sync_loop<BM, BN, BK, 2, NCW, KG, Frag>(a, ring, cw, lane, m0, n0, T, read, mma);
     } else if constexpr (LEAN) {
+        if (wr * WTM >= M - m0 || wc * WTN >= N - n0) {  // nothing of this wave's part is in C
+            WaitTally tally;
+            if (release_only<P>(T, S, fl, a.status, tally))
+                publish_tally(a.stats ? a.stats + kStatGemmConsumer : nullptr, tally);
+            return;
+        }
         constexpr int KS = BK / 16;
         struct LeanFrag {
             bf16x8 a[FM];
