@@ -93,6 +93,8 @@ VARIANTS = [
     dict(BM=128, BN=128, BK=32, producer_waves=1, consumer_waves=4),
     dict(BM=256, BN=128, BK=64, producer_waves=2, consumer_waves=4),
     dict(BM=64, BN=64, BK=32, producer_waves=1, consumer_waves=4),
+    dict(BM=64, BN=64, BK=32, producer_waves=2, consumer_waves=4),
+    dict(BM=64, BN=64, BK=32, producer_waves=4, consumer_waves=4),
     dict(BM=256, BN=128, BK=32, producer_waves=1, consumer_waves=4, flags=1),
     dict(BM=128, BN=128, BK=32, producer_waves=1, consumer_waves=4, flags=1),
     dict(BM=64, BN=64, BK=32, producer_waves=1, consumer_waves=4, flags=1),
