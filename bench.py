@@ -33,6 +33,11 @@ timed as two back-to-back regions, each bracketed by torch.cuda.synchronize()
                          buffers
   copy.direct_baseline = this library's unstaged copy of the same buffers
                          (no LDS ring, no roles), the ablation of staging
+  ring_depth_2         = for a workload whose ring depth is above 2 (bf16
+                         8192^3: S = 4), the same GEMM through the default
+                         configuration of a 2-slot ring, for context
+Each comparison leg first runs --leg-settle-ms (default 100) of untimed
+launches of its own kernel, then the warmup steps.
 Options select other workloads (--workload 4: ragged fp32, --workload 5:
 bf16 8192^3, --moe: a mixture-of-experts expert layer on the grouped GEMM,
 --attention: attention forward)
@@ -135,6 +140,18 @@ def time_region(torch, fn, steps: int):
 
 
 LAST_MEDIAN = [0.0]  # median per-launch kernel time of the latest time_region call
+
+
+def warm_leg(torch, fn, args) -> None:
+    """Untimed launches of a comparison leg before it is timed: its own settle
+    phase (--leg-settle-ms) and the warmup steps. A leg that follows another
+    kernel needs more than a few launches: on MI355X hipBLASLt's bf16 GEMM
+    read ~1170 TFLOP/s over its first 20 timed launches after 3 warmups and
+    ~1310 over the next 20, and kernels after a host pause start at a lower
+    clock."""
+    settle(torch, fn, args.leg_settle_ms)
+    for _ in range(args.warmup):
+        fn()
 
 
 def settle(torch, fn, min_ms: float) -> dict:
@@ -311,8 +328,7 @@ def run(args):
         try:
             dC_h = torch.empty_like(dC)
             hgemm = lambda: wsg.gemm_bias_relu_ex(dA, dB, dbias, dC_h, stages=stages, config=hcfg)  # noqa: E731
-            for _ in range(args.warmup):
-                hgemm()
+            warm_leg(torch, hgemm, args)
             h_wall, h_kern, h_min = time_region(torch, hgemm, args.steps)
             wsg.check_device_status()
             h_ach = flops / h_kern / 1e12
@@ -336,13 +352,32 @@ def run(args):
                     group_k=resolved["group_k"], flags=(args.flags | wsg.WSG_FLAG_NO_STREAM_K) & ~wsg.WSG_FLAG_STREAM_K)
         dC_n = torch.empty_like(dC)
         ngemm = lambda: wsg.gemm_bias_relu_ex(dA, dB, dbias, dC_n, stages=stages, config=ncfg)  # noqa: E731
-        for _ in range(args.warmup):
-            ngemm()
+        warm_leg(torch, ngemm, args)
         n_wall, n_kern, _ = time_region(torch, ngemm, args.steps)
         wsg.check_device_status()
         result["no_stream_k"] = {"kernel_tflops": round(flops / n_kern / 1e12, 3), "kernel_ms": round(n_kern * 1e3, 4),
                                  "stream_k_speedup": round(n_kern / g_kern, 4)}
         del dC_n
+
+    explicit_tile = any((args.bm, args.bn, args.bk, args.producers, args.consumers, args.group_k, args.flags))
+    if stages != 2 and not args.no_ablation and not args.homogeneous and not explicit_tile:
+        # context for a workload whose ring depth is fixed above 2: the same GEMM
+        # through the default configuration of a 2-slot ring (for bf16 256 x 256
+        # tiles that allows k tiles of 64, which a 4-slot ring does not fit)
+        d2 = wsg.resolve_config(wsg.WSG_FP32 if dtype == "fp32" else wsg.WSG_BF16, M, N, K, 2, None)
+        dC_2 = torch.empty_like(dC)
+        gemm2 = gemm_launcher(wsg, w, dA, dB, dbias, dC_2, 2, None)
+        warm_leg(torch, gemm2, args)
+        r_wall, r_kern, _ = time_region(torch, gemm2, args.steps)
+        wsg.check_device_status()
+        r_ach = flops / r_kern / 1e12
+        result["ring_depth_2"] = {
+            "stages": 2, "tile": [d2["BM"], d2["BN"], d2["BK"]], "producer_waves": d2["producer_waves"],
+            "consumer_waves": d2["consumer_waves"], "kernel_tflops": round(r_ach, 3), "frac": round(r_ach / peak, 4),
+            "kernel_ms": round(r_kern * 1e3, 4), "speedup_over_workload_stages": round(g_kern / r_kern, 4),
+            "bit_identical": bool(torch.equal(dC_2, dC)),
+        }
+        del dC_2
 
     if not args.no_vendor:
         # the vendor library (hipBLASLt through torch) on the same operands, for
@@ -354,8 +389,7 @@ def run(args):
         torch.backends.cuda.matmul.allow_tf32 = False
         try:
             vendor = lambda: torch.relu_(torch.addmm(vb, vA, vB))  # noqa: E731
-            for _ in range(args.warmup):
-                vendor()
+            warm_leg(torch, vendor, args)
             v_wall, v_kern, _ = time_region(torch, vendor, args.steps)
         finally:
             torch.backends.cuda.matmul.allow_tf32 = prev_tf32
@@ -388,7 +422,7 @@ def run(args):
         # torch's own device copy of the same buffers, timed the same way: what
         # a plain (unstaged) copy kernel reaches on this device
         plain = lambda: copy_dst.copy_(copy_src)  # noqa: E731
-        plain()
+        warm_leg(torch, plain, args)
         _, p_kern, _ = time_region(torch, plain, args.steps)
         result["copy"]["plain_device_copy"] = {"value": round(moved / p_kern / 1e9, 1), "unit": "GB/s",
                                                "kind": "torch Tensor.copy_ on the device"}
@@ -397,8 +431,7 @@ def run(args):
         # through registers in a grid-stride loop, 4 in flight), timed the same way
         direct_cfg = dict(flags=wsg.WSG_FLAG_DIRECT_COPY | (0 if args.copy_cached else wsg.WSG_FLAG_NONTEMPORAL))
         direct = lambda: wsg.staged_copy_ex(copy_src, copy_dst, stages=copy_stages, config=direct_cfg)  # noqa
-        for _ in range(args.warmup):
-            direct()
+        warm_leg(torch, direct, args)
         _, d_kern, _ = time_region(torch, direct, args.steps)
         wsg.check_device_status()
         result["copy"]["direct_baseline"] = {"value": round(moved / d_kern / 1e9, 1), "unit": "GB/s",
@@ -494,7 +527,7 @@ def run_moe(args):
     # the same flops as one dense GEMM: every row through expert 0's weights
     dC_d = torch.empty_like(dC)
     dense = lambda: wsg.gemm_bias_relu_ex(dA, dB[0], dbias[0], dC_d, stages=stages, config=config)  # noqa: E731
-    dense()
+    warm_leg(torch, dense, args)
     _, d_kern, _ = time_region(torch, dense, args.steps)
     wsg.check_device_status()
     del dC_d
@@ -657,6 +690,8 @@ def main():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--leg-settle-ms", type=float, default=100.0,
+                   help="untimed launches of each comparison leg before it is timed (ms)")
     p.add_argument("--settle-ms", type=float, default=200.0,
                    help="untimed hot-path steps for at least this long before the first warmup step")
     p.add_argument("--workload", type=int, default=3, choices=[1, 3, 4, 5])

@@ -177,8 +177,10 @@ def _gemm_operands(A, B, bias, C, want_dtype):
     return M, N, K, C
 
 
-def gemm_bias_relu(A, B, bias, C=None, stages: int = 4):
-    """C = relu(A @ B + bias) for float32 tensors; returns C."""
+def gemm_bias_relu(A, B, bias, C=None, stages: int = 2):
+    """C = relu(A @ B + bias) for float32 tensors; returns C. `stages` is the
+    LDS ring depth; the GEMM calls default to 2, the fastest depth measured on
+    MI355X for the default tiles (a deeper ring forces shallower k tiles)."""
     import torch
     M, N, K, C = _gemm_operands(A, B, bias, C, (torch.float32,))
     _use_current_stream()
@@ -191,7 +193,7 @@ def _bf16_ok():
     return (torch.bfloat16, torch.int16, torch.uint16)
 
 
-def gemm_bias_relu_bf16(A, B, bias, C=None, stages: int = 4):
+def gemm_bias_relu_bf16(A, B, bias, C=None, stages: int = 2):
     """C = relu(A @ B + bias) for bf16 tensors (or their 16-bit patterns); fp32 C."""
     M, N, K, C = _gemm_operands(A, B, bias, C, _bf16_ok())
     _use_current_stream()
@@ -200,7 +202,7 @@ def gemm_bias_relu_bf16(A, B, bias, C=None, stages: int = 4):
     return C
 
 
-def gemm_bias_relu_ex(A, B, bias, C=None, stages: int = 4, config=None):
+def gemm_bias_relu_ex(A, B, bias, C=None, stages: int = 2, config=None):
     """Either GEMM with an explicit launch configuration (Config or dict)."""
     import torch
     if A.dtype == torch.float32:
@@ -214,7 +216,7 @@ def gemm_bias_relu_ex(A, B, bias, C=None, stages: int = 4, config=None):
     return C
 
 
-def gemm_bias_relu_ex_noalloc(A, B, bias, C, stages: int = 4, config=None):
+def gemm_bias_relu_ex_noalloc(A, B, bias, C, stages: int = 2, config=None):
     """gemm_bias_relu_ex without any device allocation, by the library or
     here: C must be given; the stream-K workspace is the library's static
     per-device scratch array (calls that may overlap on one GPU race)."""
@@ -232,7 +234,7 @@ def gemm_bias_relu_ex_noalloc(A, B, bias, C, stages: int = 4, config=None):
     return C
 
 
-def grouped_gemm_bias_relu_ex(A, B, bias, group_rows, C=None, stages: int = 4, config=None):
+def grouped_gemm_bias_relu_ex(A, B, bias, group_rows, C=None, stages: int = 2, config=None):
     """Mixture-of-experts GEMM: A's rows sorted by expert, group_rows[e] of them
     for expert e; B is (experts, K, N), bias (experts, N). Returns C (rows, N)
     with C[rows of e] = relu(A[rows of e] @ B[e] + bias[e])."""
@@ -300,7 +302,7 @@ def attention_fwd(Q, K, V, O=None, scale=None, causal: bool = False, stages: int
     return O
 
 
-def resolve_config(dtype: int, M: int, N: int, K: int, stages: int = 4, config=None) -> dict:
+def resolve_config(dtype: int, M: int, N: int, K: int, stages: int = 2, config=None) -> dict:
     """The launch configuration gemm_bias_relu_ex would use (no device work)."""
     out = Config()
     _raise_on(lib.wsg_gemm_resolve_config(dtype, M, N, K, stages, _config(config), ctypes.pointer(out)))
