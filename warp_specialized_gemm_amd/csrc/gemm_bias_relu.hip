@@ -256,6 +256,54 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
         // before the wait for the next free slot, so a full signal never
         // waits on an empty one (the producer spends the steady state of a
         // compute-bound kernel blocked on empty slots).
+        // The 12-wave bf16 kernels with a ring of 4 (or more, even) slots and an
+        // even tile count: each producer step takes two slots, one empty wait per
+        // slot, the loads of both, then publishes both together once they
+        // have landed, so the per-step bookkeeping and flag traffic come once
+        // per two tiles; with 4 slots, one pair loads while the consumers read
+        // the other (measured on MI355X, bf16 8192^3 at S = 4: +2% to +5% in
+        // four interleaved runs, 1056-1116 -> 1110-1136 TFLOP/s,
+        // bit-identical). An odd tile
+        // count takes the one-slot loop below, which keeps the in-flight load
+        // counts exact.
+        if constexpr (NCW == 8 && ES == 2 && 2 * NL <= 63) {
+            if (S >= 4 && (S & 1) == 0 && (T & 1) == 0) {
+                const int D2 = max(1, min(S / 2 - 1, 63 / (2 * NL)));  // pairs in flight
+                int inflight = 0, ps = 0;
+                for (int t = 0; t < T; t += 2) {
+                    if (inflight == D2) {
+                        wait_vmcnt_dyn((D2 - 1) * 2 * NL);
+                        fl.arrive_full(ps);
+                        fl.arrive_full(ps + 1);
+                        ps = ps + 2 == S ? 0 : ps + 2;
+                        --inflight;
+                    }
+                    if (!fl.template wait_empty<NCW>(s, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+                    if (!fl.template wait_empty<NCW>(s + 1, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
+                    unsigned char *slot = ring + (size_t)s * SLOT;
+                    const int64_t k0 = (int64_t)t * BK;
+                    ad.issue(slot, wave, A_rows, rows_valid, K, k0);
+                    bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
+                    ad.issue(slot + SLOT, wave, A_rows, rows_valid, K, k0 + BK);
+                    bd.issue(slot + SLOT + A_BYTES, wave, a.B, N, K, n0, k0 + BK);
+                    ++inflight;
+                    s += 2;
+                    if (s == S) {
+                        s = 0;
+                        ++lap;
+                    }
+                }
+                while (inflight > 0) {
+                    wait_vmcnt_dyn((inflight - 1) * 2 * NL);
+                    fl.arrive_full(ps);
+                    fl.arrive_full(ps + 1);
+                    ps = ps + 2 == S ? 0 : ps + 2;
+                    --inflight;
+                }
+                publish_tally(a.stats ? a.stats + kStatGemmProducer : nullptr, tally);
+                return;
+            }
+        }
         const int D = max(1, min(S - 1, 63 / NL));
         int inflight = 0, ps = 0;  // tiles issued but not published; slot of the oldest
         for (int t = 0; t < T; ++t) {
