@@ -129,11 +129,12 @@ def test_variants_and_stages_integer_bit_exact(gpu, config, stages):
     assert np.array_equal(C.astype(np.float64), oracle.gemm_bias_relu(A, B, bias))
 
 
-@pytest.mark.parametrize("K", [16, 32 * 7, 32 * 8, 32 * 9 + 8])
+@pytest.mark.parametrize("K", [0, 16, 32 * 7, 32 * 8, 32 * 9 + 8])
 def test_four_slot_ring_even_and_odd_tile_counts(gpu, K):
     """At S = 4 the 256 x 256 x 32 producers fill two slots per step when the k
-    tile count is even and one slot per step when it is odd (here 1, 7, 8 and
-    10 tiles, the last one 8 deep); both give the oracle's integers exactly."""
+    tile count is even and one slot per step when it is odd (here 0, 1, 7, 8
+    and 10 tiles, the last one 8 deep); both give the oracle's integers
+    exactly."""
     M, N = 300, 520
     A, B, bias = int_case(2100 + K, M, N, K)
     config = dict(BM=256, BN=256, BK=32, producer_waves=4, consumer_waves=8)
