@@ -257,15 +257,16 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
         // waits on an empty one (the producer spends the steady state of a
         // compute-bound kernel blocked on empty slots).
         // The 12-wave bf16 kernels with a ring of 4 (or more, even) slots and an
-        // even tile count: each producer step takes two slots, one empty wait per
-        // slot and the loads of both, then publishes each slot as its loads
-        // land, so the per-step bookkeeping comes once per two tiles; with 4
-        // slots, one pair loads while the consumers read the other (measured
-        // on MI355X, bf16 8192^3 at S = 4: +2% to +5% in four interleaved
-        // runs, 1056-1116 -> 1110-1136 TFLOP/s, and publishing each slot as it
-        // lands rather than both together +1.2% more; bit-identical). An odd
-        // tile count takes the one-slot loop below, which keeps the in-flight
-        // load counts exact.
+        // even tile count: each producer step takes two slots, issuing each
+        // slot's loads as soon as that slot is free, then publishes each slot
+        // as its loads land, so the per-step bookkeeping comes once per two
+        // tiles; with 4 slots, one pair loads while the consumers read the
+        // other (measured on MI355X, bf16 8192^3 at S = 4, interleaved runs,
+        // bit-identical: +2% to +5% with both slots waited for, loaded and
+        // published together, 1056-1116 -> 1110-1136 TFLOP/s; +1.2% more with
+        // each published as it lands; +2.6% to +4.6% more, 1118-1137 ->
+        // 1167-1169, with each loaded once free). An odd tile count takes the
+        // one-slot loop below, which keeps the in-flight load counts exact.
         if constexpr (NCW == 8 && ES == 2 && 2 * NL <= 63) {
             if (S >= 4 && (S & 1) == 0 && (T & 1) == 0) {
                 const int D2 = max(1, min(S / 2 - 1, 63 / (2 * NL)));  // pairs in flight
@@ -280,11 +281,11 @@ __device__ __forceinline__ void produce(const GemmArgs &a, unsigned char *ring, 
                         --inflight;
                     }
                     if (!fl.template wait_empty<NCW>(s, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
-                    if (!fl.template wait_empty<NCW>(s + 1, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
                     unsigned char *slot = ring + (size_t)s * SLOT;
                     const int64_t k0 = (int64_t)t * BK;
                     ad.issue(slot, wave, A_rows, rows_valid, K, k0);
                     bd.issue(slot + A_BYTES, wave, a.B, N, K, n0, k0);
+                    if (!fl.template wait_empty<NCW>(s + 1, (lap & 1u) ^ 1u, a.status, kStatusGemm, tally)) return;
                     ad.issue(slot + SLOT, wave, A_rows, rows_valid, K, k0 + BK);
                     bd.issue(slot + SLOT + A_BYTES, wave, a.B, N, K, n0, k0 + BK);
                     ++inflight;
